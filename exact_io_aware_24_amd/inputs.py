@@ -1,0 +1,100 @@
+"""Seeded synthetic attention inputs.
+
+This module holds the workload shapes and the random-input recipe, and
+nothing of the attention arithmetic: both the GPU library's tests and the
+CPU oracle's tests draw their Q, K, V from here, and nothing else is shared
+between the two.
+
+The pages measure on no dataset; the workloads are synthetic by design:
+
+* Q, K, V are drawn as ``torch.randn`` in float32 from a CPU generator
+  seeded once per call (default seed 1234), in the order q, k, v;
+* the outlier workload additionally picks, for Q and then for K, for every
+  (batch, head) in order, ``floor(0.05 * N)`` distinct rows with
+  ``torch.randperm`` from the same generator and multiplies those whole rows
+  by 20 (V is left alone);
+* the result is rounded to bfloat16 (round-to-nearest-even, torch's
+  ``.to``) for the bf16 workloads; the tiny exactness case stays float32.
+
+The same seed therefore gives bit-identical inputs on every machine with the
+same torch version.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+DEFAULT_SEED = 1234
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention problem: ``[B, H, N, d]`` Q/K/V, optional causal mask."""
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str  # "bf16" or "fp32": the type Q, K, V are stored in
+    outliers: bool = False  # 5 % of Q and K rows scaled by 20
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic FLOPs, 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def describe(self) -> str:
+        return "B=%d,H=%d,N=%d,d=%d,%s,%s%s" % (
+            self.B, self.H, self.N, self.d,
+            "causal" if self.causal else "non-causal", self.dtype,
+            ",5%-rows-x20-outliers" if self.outliers else "")
+
+
+# The five workloads.  The tiny float32 case checks exactness; the causal
+# N=8192, d=128 case is the headline throughput workload.
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_fp32_n128_d64", 1, 1, 128, 64, False, "fp32"),
+        Workload("train_b8h16_n2048_d64", 8, 16, 2048, 64, False, "bf16"),
+        Workload("causal_b2h16_n8192_d128", 2, 16, 8192, 128, True, "bf16"),
+        Workload("longseq_causal_b1h16_n32768_d128", 1, 16, 32768, 128, True, "bf16"),
+        Workload("outlier_b4h32_n4096_d128", 4, 32, 4096, 128, False, "bf16",
+                 outliers=True),
+    ]
+}
+HEADLINE = "causal_b2h16_n8192_d128"
+
+
+def make_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16",
+                seed: int = DEFAULT_SEED, outliers: bool = False):
+    """Return CPU tensors ``(q, k, v)`` of shape ``[B, H, N, d]``."""
+    if dtype not in ("bf16", "fp32"):
+        raise ValueError("dtype must be 'bf16' or 'fp32'")
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    k = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    if outliers:
+        n_out = int(math.floor(0.05 * N))
+        for t in (q, k):
+            for b in range(B):
+                for h in range(H):
+                    rows = torch.randperm(N, generator=g)[:n_out]
+                    t[b, h, rows] *= 20.0
+    if dtype == "bf16":
+        q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    return q, k, v
+
+
+def workload_inputs(w: Workload, seed: int = DEFAULT_SEED):
+    """Inputs of a named workload (CPU tensors)."""
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed=seed,
+                       outliers=w.outliers)

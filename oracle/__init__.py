@@ -1,0 +1,191 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never links, loads or
+calls it, and it shares no code with the GPU path.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, IEEE double precision,
+POSIX threads over independent query rows); this module only builds it with
+gcc and marshals numpy arrays into it.  What is computed, and the page passage
+each step follows, is stated in the C file's header:
+
+* ``S = scale * Q K^T`` row by row, causal keys ``j > i`` at ``-inf``;
+* ``P = softmax(S)`` with the row maximum subtracted first;
+* ``O = P V`` and ``lse = m + ln(sum exp(S - m))`` (natural log).
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms,
+invariants, the two-block merge rule from the online-softmax section of the
+"Large language models part 06" page, and brute force on tiny shapes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle's C source into a shared library with gcc.
+
+    -O2 without fast-math and with ``-ffp-contract=off``: the compiler may not
+    reassociate or fuse the double-precision arithmetic, so the oracle is the
+    written definition evaluated in IEEE order.  ``src``/``out`` exist so the
+    tests can also build deliberately broken copies of the oracle and check
+    that its pins catch them.
+    """
+    if not force and os.path.exists(out):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-pthread", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _f64(a) -> np.ndarray:
+    """Any array-like (numpy, or a CPU torch tensor of any float dtype) to a
+    C-contiguous float64 numpy array holding exactly the same values."""
+    if hasattr(a, "detach"):  # torch tensor: widen on the torch side first,
+        a = a.detach().cpu()  # numpy has no bfloat16
+        import torch
+        a = a.to(torch.float64).numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+class OracleLib:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.oracle_attention_f64.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64,
+                                             i64, ctypes.c_double, ctypes.c_int,
+                                             ctypes.c_int]
+        lib.oracle_attention_f64.restype = ctypes.c_int
+        lib.oracle_attention_rows_f64.argtypes = [
+            dp, ctypes.POINTER(i64), i64, dp, dp, i64, i64, ctypes.c_double,
+            ctypes.c_int, dp, dp, ctypes.c_int]
+        lib.oracle_attention_rows_f64.restype = ctypes.c_int
+        lib.oracle_probs_f64.argtypes = [dp, dp, i64, i64, i64, ctypes.c_double,
+                                         ctypes.c_int, dp, dp, dp]
+        lib.oracle_probs_f64.restype = ctypes.c_int
+        lib.oracle_default_threads.argtypes = []
+        lib.oracle_default_threads.restype = ctypes.c_int
+        self.path = path
+        self._lib = lib
+
+    def default_threads(self) -> int:
+        """Host cores this process may run on (``sched_getaffinity``)."""
+        return int(self._lib.oracle_default_threads())
+
+    def attention(self, q, k, v, scale: float, causal: bool = False,
+                  nthreads: int = 0):
+        """Exact attention of every head.
+
+        ``q``: ``[..., Nq, d]``; ``k``, ``v``: ``[..., Nk, d]`` with the same
+        leading (head) dimensions.  Returns ``(o, lse, threads_used)`` with
+        ``o`` ``[..., Nq, d]`` and ``lse`` ``[..., Nq]``, both float64.
+        """
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        if q.ndim < 2 or k.shape != v.shape or q.shape[:-2] != k.shape[:-2] \
+                or q.shape[-1] != k.shape[-1]:
+            raise ValueError("shape mismatch: q %s k %s v %s"
+                             % (q.shape, k.shape, v.shape))
+        lead = q.shape[:-2]
+        nq, d = q.shape[-2], q.shape[-1]
+        nk = k.shape[-2]
+        nh = int(np.prod(lead)) if lead else 1
+        o = np.empty(q.shape, dtype=np.float64)
+        lse = np.empty(lead + (nq,), dtype=np.float64)
+        rc = self._lib.oracle_attention_f64(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), nh, nq, nk, d,
+            float(scale), int(bool(causal)), int(nthreads))
+        if rc < 0:
+            raise RuntimeError("oracle_attention_f64 failed (%d)" % rc)
+        return o, lse, rc
+
+    def attention_rows(self, q_rows, rows, k, v, scale: float,
+                       causal: bool = False, nthreads: int = 0):
+        """Exact attention of selected query rows of ONE head.
+
+        ``q_rows``: ``[R, d]`` query vectors, ``rows``: ``[R]`` their row
+        indices (the causal mask needs them), ``k``, ``v``: ``[Nk, d]``.
+        Returns ``(o [R, d], lse [R], threads_used)``.
+        """
+        q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        if q_rows.ndim != 2 or rows.shape != (q_rows.shape[0],) or k.ndim != 2 \
+                or k.shape != v.shape or k.shape[1] != q_rows.shape[1]:
+            raise ValueError("shape mismatch")
+        nr, d = q_rows.shape
+        o = np.empty((nr, d), dtype=np.float64)
+        lse = np.empty((nr,), dtype=np.float64)
+        rc = self._lib.oracle_attention_rows_f64(
+            _ptr(q_rows), rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            nr, _ptr(k), _ptr(v), k.shape[0], d, float(scale),
+            int(bool(causal)), _ptr(o), _ptr(lse), int(nthreads))
+        if rc < 0:
+            raise RuntimeError("oracle_attention_rows_f64 failed (%d)" % rc)
+        return o, lse, rc
+
+    def probs(self, q, k, scale: float, causal: bool = False):
+        """The probability matrix of ONE head: ``(P [Nq, Nk], m [Nq], l [Nq])``
+        where ``m`` is each row's maximum score and ``l = sum_j exp(s_j - m)``.
+        """
+        q, k = _f64(q), _f64(k)
+        if q.ndim != 2 or k.ndim != 2 or q.shape[1] != k.shape[1]:
+            raise ValueError("shape mismatch")
+        nq, nk, d = q.shape[0], k.shape[0], q.shape[1]
+        p = np.empty((nq, nk), dtype=np.float64)
+        m = np.empty((nq,), dtype=np.float64)
+        l = np.empty((nq,), dtype=np.float64)
+        rc = self._lib.oracle_probs_f64(_ptr(q), _ptr(k), nq, nk, d,
+                                        float(scale), int(bool(causal)),
+                                        _ptr(p), _ptr(m), _ptr(l))
+        if rc < 0:
+            raise RuntimeError("oracle_probs_f64 failed (%d)" % rc)
+        return p, m, l
+
+
+def _default() -> OracleLib:
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or (
+                    os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+                build(force=True)
+            _lib = OracleLib(_LIB_PATH)
+        return _lib
+
+
+def default_threads() -> int:
+    return _default().default_threads()
+
+
+def attention(q, k, v, scale: float, causal: bool = False, nthreads: int = 0):
+    return _default().attention(q, k, v, scale, causal, nthreads)
+
+
+def attention_rows(q_rows, rows, k, v, scale: float, causal: bool = False,
+                   nthreads: int = 0):
+    return _default().attention_rows(q_rows, rows, k, v, scale, causal,
+                                     nthreads)
+
+
+def probs(q, k, scale: float, causal: bool = False):
+    return _default().probs(q, k, scale, causal)

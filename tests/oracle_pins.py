@@ -1,0 +1,308 @@
+"""Pins for the fp64 attention oracle.
+
+Each ``pin_*`` function takes an oracle object (``oracle.OracleLib``) and
+raises ``AssertionError`` when the oracle disagrees with something fixed
+outside the oracle itself: a closed form, an invariant of softmax attention,
+the two-block merge rule printed on the pages, or a brute-force evaluation
+written differently (no max subtraction, ``math.fsum``) on tiny inputs.
+
+The same functions run against the real oracle (``test_oracle_pins.py``) and
+against deliberately broken copies of it (``test_oracle_mutants.py``), which
+shows that each plausible mistake is caught by at least one pin.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, tol=TOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b)), what
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    assert err <= tol * scale, "%s: max |diff| %.3e" % (what, err)
+
+
+# ---------------------------------------------------------------------------
+# softmax step
+
+
+def pin_rows_sum_to_one(orc):
+    """Every probability row is non-negative and sums to 1; masked entries
+    (causal, key after query) are exactly 0."""
+    r = _rng(1)
+    for causal in (False, True):
+        q = r.standard_normal((37, 16))
+        k = r.standard_normal((37, 16)) * 3
+        p, m, l = orc.probs(q, k, 0.25, causal)
+        assert np.all(p >= 0)
+        _close(p.sum(axis=1), np.ones(37), what="row sums")
+        if causal:
+            assert np.all(np.triu(p, 1) == 0.0), "masked entries non-zero"
+            assert np.all(np.diag(p) > 0), "diagonal masked"
+
+
+def pin_probs_closed_form_two_keys(orc):
+    """Two keys: p = logistic(s1 - s2), the textbook closed form; the row
+    maximum and l = 1 + exp(-|s1 - s2|) follow as well."""
+    q = np.array([[1.5, -0.5, 2.0]])
+    k = np.array([[0.3, 1.0, -0.7], [-1.2, 0.4, 0.9]])
+    scale = 0.7
+    s = [scale * float(np.dot(q[0], k[j])) for j in range(2)]
+    p, m, l = orc.probs(q, k, scale, False)
+    p0 = 1.0 / (1.0 + math.exp(s[1] - s[0]))
+    _close(p[0], [p0, 1.0 - p0], what="two-key probabilities")
+    _close(m, [max(s)], what="row max")
+    _close(l, [1.0 + math.exp(-abs(s[0] - s[1]))], what="row l")
+
+
+# ---------------------------------------------------------------------------
+# whole pipeline: closed forms
+
+
+def pin_zero_query_is_mean_of_v(orc):
+    """Q = 0 makes every score 0: attention is uniform over the visible keys,
+    so O is the mean of V (causal: the mean of rows 0..i) and lse = ln(count).
+    scale = 0 with any Q gives the same."""
+    r = _rng(2)
+    n, d = 23, 8
+    v = r.standard_normal((1, n, d))
+    k = r.standard_normal((1, n, d))
+    for q, scale in ((np.zeros((1, n, d)), 0.37),
+                     (r.standard_normal((1, n, d)), 0.0)):
+        o, lse, _ = orc.attention(q, k, v, scale, False)
+        _close(o[0], np.broadcast_to(v[0].mean(axis=0), (n, d)), what="mean V")
+        _close(lse[0], np.full(n, math.log(n)), what="ln N")
+        o, lse, _ = orc.attention(q, k, v, scale, True)
+        prefix = np.cumsum(v[0], axis=0) / np.arange(1, n + 1)[:, None]
+        _close(o[0], prefix, what="prefix mean V")
+        _close(lse[0], np.log(np.arange(1, n + 1)), what="ln(i+1)")
+
+
+def pin_constant_v_column(orc):
+    """A V column that is the same constant for every key comes out
+    unchanged in every output row (the weights sum to 1)."""
+    r = _rng(3)
+    n, d = 31, 6
+    q = r.standard_normal((2, n, d)) * 2
+    k = r.standard_normal((2, n, d)) * 2
+    v = r.standard_normal((2, n, d))
+    v[:, :, 2] = -3.25
+    v[:, :, 5] = 7.0
+    for causal in (False, True):
+        o, _, _ = orc.attention(q, k, v, 0.5, causal)
+        _close(o[:, :, 2], np.full((2, n), -3.25), what="const col 2")
+        _close(o[:, :, 5], np.full((2, n), 7.0), what="const col 5")
+
+
+def pin_single_key(orc):
+    """With one key the only weight is 1: O = v_0 and lse = scale*q.k_0."""
+    r = _rng(4)
+    d = 5
+    q = r.standard_normal((3, 1, d))
+    k = r.standard_normal((3, 1, d))
+    v = r.standard_normal((3, 1, d))
+    o, lse, _ = orc.attention(q, k, v, 1.3, False)
+    _close(o, v, what="O = V")
+    _close(lse[:, 0], 1.3 * np.einsum("hd,hd->h", q[:, 0], k[:, 0]),
+           what="lse = scale q.k")
+
+
+def pin_dominant_key(orc):
+    """When one key's score exceeds all others by > 750 every other weight
+    underflows to exactly 0 in double precision: O is that key's V row and
+    lse is its score (no overflow even for scores near 1e4)."""
+    d, n = 4, 9
+    k = np.zeros((1, n, d))
+    for j in range(n):
+        k[0, j, 0] = float(j)  # key j has first component j
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = 1000.0
+    v = np.arange(n * d, dtype=np.float64).reshape(1, n, d)
+    o, lse, _ = orc.attention(q, k, v, 1.0, False)
+    _close(o[0, 0], v[0, n - 1], what="dominant key O")
+    _close(lse[0], [1000.0 * (n - 1)], what="dominant key lse")
+
+
+# ---------------------------------------------------------------------------
+# invariants
+
+
+def pin_key_shift(orc):
+    """Adding one vector u to every key adds scale*q_i.u to every score of
+    row i: O is unchanged and lse moves by exactly that amount."""
+    r = _rng(5)
+    n, d = 19, 7
+    q = r.standard_normal((1, n, d))
+    k = r.standard_normal((1, n, d))
+    v = r.standard_normal((1, n, d))
+    u = r.standard_normal(d) * 2
+    for causal in (False, True):
+        o1, l1, _ = orc.attention(q, k, v, 0.6, causal)
+        o2, l2, _ = orc.attention(q, k + u, v, 0.6, causal)
+        _close(o2, o1, tol=1e-11, what="shift O")
+        _close(l2[0] - l1[0], 0.6 * (q[0] @ u), tol=1e-11, what="shift lse")
+
+
+def pin_key_permutation(orc):
+    """Without a mask attention is a sum over keys: permuting the K and V
+    rows together leaves O and lse unchanged."""
+    r = _rng(6)
+    n, d = 29, 8
+    q = r.standard_normal((2, n, d))
+    k = r.standard_normal((2, n, d))
+    v = r.standard_normal((2, n, d))
+    perm = r.permutation(n)
+    o1, l1, _ = orc.attention(q, k, v, 0.4, False)
+    o2, l2, _ = orc.attention(q, k[:, perm], v[:, perm], 0.4, False)
+    _close(o2, o1, what="perm O")
+    _close(l2, l1, what="perm lse")
+
+
+def pin_causal_consistency(orc):
+    """The causal mask hides nothing from the last row and everything but
+    key 0 from row 0."""
+    r = _rng(7)
+    n, d = 17, 6
+    q = r.standard_normal((1, n, d))
+    k = r.standard_normal((1, n, d))
+    v = r.standard_normal((1, n, d))
+    oc, lc, _ = orc.attention(q, k, v, 0.8, True)
+    on, ln, _ = orc.attention(q, k, v, 0.8, False)
+    _close(oc[0, n - 1], on[0, n - 1], what="last row")
+    _close(lc[0, n - 1], ln[0, n - 1], what="last row lse")
+    _close(oc[0, 0], v[0, 0], what="row 0 = v0")
+    _close(lc[0, 0], 0.8 * (q[0, 0] @ k[0, 0]), what="row 0 lse")
+    # causal row i equals non-causal attention over the prefix 0..i
+    for i in (3, 9):
+        op, lp, _ = orc.attention(q[:, i:i + 1], k[:, :i + 1], v[:, :i + 1],
+                                  0.8, False)
+        _close(oc[0, i], op[0, 0], what="prefix row %d" % i)
+        _close(lc[0, i], lp[0, 0], what="prefix lse %d" % i)
+
+
+# ---------------------------------------------------------------------------
+# the online-softmax merge printed on the pages
+
+
+def merge_blocks(orc, q, k, v, scale, bounds):
+    """Fold per-block results with the two-block merge rule of the online
+    softmax section: m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m),
+    O = O1 (l1 e^(m1-m) / l) + O2 (e^(m2-m) / l), where O1 is the normalised
+    output so far and O2 the new block's unnormalised sum P~2 V."""
+    m_acc = l_acc = o_acc = None
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        kb, vb = k[lo:hi], v[lo:hi]
+        ob, _, _ = orc.attention(q[None], kb[None], vb[None], scale, False)
+        _, mb, lb = orc.probs(q, kb, scale, False)
+        ob = ob[0] * lb[:, None]  # unnormalised block output P~ V
+        if m_acc is None:
+            m_acc, l_acc, o_acc = mb, lb, ob / lb[:, None]
+            continue
+        m_new = np.maximum(m_acc, mb)
+        a1 = np.exp(m_acc - m_new)
+        a2 = np.exp(mb - m_new)
+        l_new = l_acc * a1 + lb * a2
+        o_acc = o_acc * (l_acc * a1 / l_new)[:, None] + ob * (a2 / l_new)[:, None]
+        m_acc, l_acc = m_new, l_new
+    return o_acc, m_acc + np.log(l_acc)
+
+
+def pin_online_merge(orc):
+    """Splitting each row's keys into 2..8 blocks at random points and
+    folding the blocks with the printed merge rule gives the full result."""
+    r = _rng(8)
+    n, d = 64, 12
+    q = r.standard_normal((n, d)) * 2
+    k = r.standard_normal((n, d)) * 2
+    v = r.standard_normal((n, d))
+    o_full, l_full, _ = orc.attention(q[None], k[None], v[None], 0.5, False)
+    for nblocks in (2, 3, 5, 8):
+        cuts = np.sort(r.choice(np.arange(1, n), nblocks - 1, replace=False))
+        bounds = [0] + list(cuts) + [n]
+        o_m, l_m = merge_blocks(orc, q, k, v, 0.5, bounds)
+        _close(o_m, o_full[0], what="merge O (%d blocks)" % nblocks)
+        _close(l_m, l_full[0], what="merge lse (%d blocks)" % nblocks)
+
+
+# ---------------------------------------------------------------------------
+# brute force
+
+
+def brute_force(q, k, v, scale, causal):
+    """sum_j e^(s_ij) v_j / sum_j e^(s_ij), summed with math.fsum, with no
+    maximum subtracted (inputs are kept small so nothing overflows)."""
+    nq, d = q.shape
+    nk = k.shape[0]
+    o = np.zeros((nq, d))
+    lse = np.zeros(nq)
+    for i in range(nq):
+        w = []
+        for j in range(nk):
+            if causal and j > i:
+                continue
+            s = scale * math.fsum(float(q[i, c]) * float(k[j, c]) for c in range(d))
+            w.append((j, math.exp(s)))
+        z = math.fsum(x for _, x in w)
+        for c in range(d):
+            o[i, c] = math.fsum(x * float(v[j, c]) for j, x in w) / z
+        lse[i] = math.log(z)
+    return o, lse
+
+
+def pin_brute_force(orc):
+    """Tiny shapes, including Nq != Nk and d != N, against the brute force."""
+    r = _rng(9)
+    for (nq, nk, d, causal) in ((1, 1, 1, False), (5, 5, 3, True),
+                                (7, 11, 4, False), (16, 16, 8, True),
+                                (16, 16, 8, False), (9, 4, 2, False)):
+        q = r.standard_normal((nq, d))
+        k = r.standard_normal((nk, d))
+        v = r.standard_normal((nk, d))
+        if causal and nq > nk:
+            continue
+        o, lse, _ = orc.attention(q[None], k[None], v[None], 0.45, causal)
+        ob, lb = brute_force(q, k, v, 0.45, causal)
+        _close(o[0], ob, what="brute O %s" % ((nq, nk, d, causal),))
+        _close(lse[0], lb, what="brute lse %s" % ((nq, nk, d, causal),))
+
+
+def pin_rows_match_full(orc):
+    """The selected-rows entry point gives the same rows as the full one."""
+    r = _rng(10)
+    n, d = 50, 8
+    q = r.standard_normal((n, d))
+    k = r.standard_normal((n, d))
+    v = r.standard_normal((n, d))
+    rows = np.array([0, 1, 13, 48, 49, 7])
+    for causal in (False, True):
+        o, lse, _ = orc.attention(q[None], k[None], v[None], 0.3, causal)
+        orow, lrow, _ = orc.attention_rows(q[rows], rows, k, v, 0.3, causal)
+        _close(orow, o[0, rows], tol=0, what="rows O")
+        _close(lrow, lse[0, rows], tol=0, what="rows lse")
+
+
+ALL_PINS = [
+    pin_rows_sum_to_one,
+    pin_probs_closed_form_two_keys,
+    pin_zero_query_is_mean_of_v,
+    pin_constant_v_column,
+    pin_single_key,
+    pin_dominant_key,
+    pin_key_shift,
+    pin_key_permutation,
+    pin_causal_consistency,
+    pin_online_merge,
+    pin_brute_force,
+    pin_rows_match_full,
+]

@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check
+that the pins catch every one of them.
+
+Each mutant is the oracle's C source with one textual change, compiled into
+a temporary library; the real oracle is untouched.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+
+MUTANTS = [
+    ("scale dropped", "p[j] = scale * dot;", "p[j] = dot;"),
+    ("scale squared", "p[j] = scale * dot;", "p[j] = scale * scale * dot;"),
+    ("max added instead of subtracted", "p[j] = exp(p[j] - m);",
+     "p[j] = exp(p[j] + m);"),
+    ("no normalisation", "        p[j] /= l;", "        p[j] /= 1.0;"),
+    ("causal mask off by one (j >= i)", "if (causal && j > i)",
+     "if (causal && j >= i)"),
+    ("causal mask missing", "if (causal && j > i)", "if (0 && j > i)"),
+    ("lse in base 2", "m + log(l)", "m + log2(l)"),
+    ("lse without the max", "m + log(l)", "log(l)"),
+    ("last feature dropped from the dot", "for (int64_t c = 0; c < d; ++c)\n            dot",
+     "for (int64_t c = 0; c + 1 < d; ++c)\n            dot"),
+    ("keys read in reverse order", "const double *kj = k + j * d;",
+     "const double *kj = k + (nk - 1 - j) * d;"),
+    ("V rows read in reverse order", "const double *vj = v + j * d;",
+     "const double *vj = v + (jend - 1 - j) * d;"),
+    ("PV sum stops one key early", "int64_t jend = (causal && i + 1 < nk) ? i + 1 : nk;",
+     "int64_t jend = (causal && i + 1 < nk) ? i : nk - 1;"),
+    ("max taken as min", "if (p[j] > m)", "if (p[j] < m && p[j] > -INFINITY)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not unique/found: %r" % old
+    mut = tmp_path / "mutant.c"
+    mut.write_text(src.replace(old, new))
+    lib = oracle.build(src=str(mut), out=str(tmp_path / "libmutant.so"))
+    orc = oracle.OracleLib(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, RuntimeError, FloatingPointError,
+                OverflowError):
+            caught.append(pin.__name__)
+    assert caught, "mutant %r passed every pin" % name
