@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention forward kernel on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one call of ``fa2_fwd`` (bf16 in, bf16 out, with lse) on the
+headline workload B=2, H=16, N=8192, d=128, causal, inputs resident in HBM.
+W untimed warm-up steps are followed by exactly K timed steps between HIP
+events on the stream the kernel is launched on.  Rank 0 prints one JSON line:
+TFLOP/s (4*B*H*N^2*d, halved for causal), the roofline of the kernel against
+the bf16 dense MFMA peak, the HBM traffic measured by rocprofv3 counters
+(when the committed counter summary matches the current kernel source), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+Only one GPU is used: ``--gpus`` above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_24_amd", "csrc", "fa2_fwd_bf16.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def score_matrix_bytes(B: int, H: int, N: int, elem_bytes: int = 2) -> float:
+    """Bytes of the N x N score matrix standard attention would write per
+    (batch, head), summed over B*H -- what the tiled kernel never stores."""
+    return float(B) * H * N * N * elem_bytes
+
+
+def compulsory_bytes(B, H, N, d, in_bytes=2, out_bytes=2, lse=True) -> float:
+    """Q, K, V read once, O (and lse) written once."""
+    n = float(B) * H * N * d
+    return 3 * n * in_bytes + n * out_bytes + (float(B) * H * N * 4 if lse else 0)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading on
+    a copy of known size), or None when there is none or it was taken on a
+    different kernel source."""
+    path = os.path.join(PROFILES, "counters_fa2_fwd_bf16_%s.md" % workload_name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            vals[key.strip()] = val.strip().strip("`")
+    try:
+        if vals.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        fetch = float(vals["fetch_bytes_per_launch"])
+        write = float(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+    return fetch + write
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the
+    workload: whole heads, all their rows, as many heads as fit the budget
+    after a one-head calibration on a row subset."""
+    import numpy as np
+    import oracle
+    BH = w.B * w.H
+    qf, kf, vf = (t.reshape(BH, w.N, w.d) for t in (q, k, v))
+
+    def head_flops(rows):
+        keys = (rows + 1) if w.causal else np.full(rows.shape, w.N)
+        return float(np.sum(4.0 * w.d * keys))
+
+    # calibration: every 16th row of head 0
+    rows = np.arange(0, w.N, 16, dtype=np.int64)
+    t0 = time.perf_counter()
+    _, _, threads = oracle.attention_rows(qf[0, rows], rows, kf[0], vf[0],
+                                          w.scale, w.causal)
+    rate = head_flops(rows) / max(time.perf_counter() - t0, 1e-9)
+    all_rows = np.arange(w.N, dtype=np.int64)
+    per_head = head_flops(all_rows)
+    n_heads = int(max(1, min(BH, round(budget_s * rate / per_head))))
+    t0 = time.perf_counter()
+    for h in range(n_heads):
+        _, _, threads = oracle.attention(qf[h:h + 1], kf[h:h + 1], vf[h:h + 1],
+                                         w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    flops = per_head * n_heads
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "%d of %d heads (all %d query rows each) of %s; fp64 C oracle, "
+                  "%.1f s wall, %.3g flop counted like the GPU metric"
+                  % (n_heads, BH, w.N, w.describe(), dt, flops),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: the headline workload)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter "
+                         "calibration runs)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only (this build runs no multi-GPU "
+              "path); got --gpus %d" % args.gpus, file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_io_aware_24_amd as fa2
+    from exact_io_aware_24_amd import inputs as wl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    name = args.workload or wl.HEADLINE
+    w = wl.WORKLOADS[name]
+    if w.dtype != "bf16":
+        print("the benchmark times the bf16 path", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    q, k, v = wl.workload_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+
+    def step():
+        fa2.forward(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+
+    traffic = read_traffic(name)
+    rec = {
+        "metric": "attention fwd TFLOP/s (1 MI355X) and % of bf16 MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded randn, bf16)",
+        "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale,
+                   "flops_per_step": w.flops, "entry_point": "fa2_fwd"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "score_matrix_bytes_not_written": score_matrix_bytes(w.B, w.H, w.N),
+        "compulsory_hbm_bytes": compulsory_bytes(w.B, w.H, w.N, w.d),
+        "kernel_source_sha256": kernel_source_hash(),
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

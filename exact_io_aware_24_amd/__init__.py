@@ -1,0 +1,161 @@
+"""MI355X-native exact attention forward (FlashAttention-2 order) -- Python
+binding of the C-ABI library ``libfa2.so`` (declared in ``include/fa2.h``).
+
+This module only marshals arguments: it checks tensor device/dtype/shape,
+passes raw device pointers and torch's current HIP stream to the library, and
+turns non-zero return codes into exceptions.  Every step of the computation
+runs in the library's HIP kernels; there is no fallback.  If the library has
+not been built (``python -m exact_io_aware_24_amd.build``) any call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+from . import inputs  # noqa: F401  (seeded synthetic workloads)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa2.so")
+
+# Return codes, mirrored from include/fa2.h.
+FA2_OK = 0
+FA2_ERR_NULL = -1
+FA2_ERR_SHAPE = -2
+FA2_ERR_HEADDIM = -3
+FA2_ERR_SCALE = -4
+FA2_ERR_ALIGN = -5
+FA2_ERR_ALIAS = -6
+FA2_ERR_HIP = -7
+
+# Every symbol include/fa2.h declares.
+EXPORTED = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_fp32", "fa2_strerror",
+            "fa2_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FA2Error(RuntimeError):
+    """A non-zero return code from the library."""
+
+    def __init__(self, code: int, func: str):
+        self.code = code
+        super().__init__("%s failed: %s (code %d)" % (func, strerror(code), code))
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libfa2.so`` (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libfa2.so is not built: run `python -m exact_io_aware_24_amd.build`"
+                " (there is no non-HIP fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        sig = [vp, vp, vp, vp, vp, i, i, i, i, ctypes.c_float, i, vp]
+        for name in ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_fp32"):
+            f = getattr(L, name)
+            f.argtypes = sig
+            f.restype = ctypes.c_int
+        L.fa2_strerror.argtypes = [i]
+        L.fa2_strerror.restype = ctypes.c_char_p
+        L.fa2_version.argtypes = []
+        L.fa2_version.restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def strerror(code: int) -> str:
+    return lib().fa2_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return int(lib().fa2_version())
+
+
+def _check_tensors(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch.Tensor" % name)
+        if t.dim() != 4:
+            raise ValueError("%s must be [B, H, N, d], got %s" % (name, tuple(t.shape)))
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v shapes differ: %s %s %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v dtypes differ")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must be bfloat16 or float32, got %s" % q.dtype)
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v are on different devices")
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None,
+            out_dtype=None, out=None, lse=None, return_lse: bool = True):
+    """Exact attention forward: ``softmax(scale * q k^T [+ causal mask]) v``.
+
+    ``q, k, v``: contiguous GPU tensors ``[B, H, N, d]``, d in {64, 128},
+    all bfloat16 (MFMA path) or all float32 (fp32 path).
+    ``out_dtype``: for bf16 inputs, ``torch.bfloat16`` (default, entry point
+    ``fa2_fwd``) or ``torch.float32`` (``fa2_fwd_o32``); float32 inputs give
+    float32 output (``fa2_fwd_fp32``).  ``scale`` defaults to ``1/sqrt(d)``.
+    ``out`` / ``lse`` may be preallocated.  Returns ``(o, lse)`` (``lse`` is
+    float32 ``[B, H, N]``, or None when ``return_lse`` is False).
+    The kernel is enqueued on torch's current stream.
+    """
+    import torch
+    _check_tensors(q, k, v)
+    B, H, N, d = (int(x) for x in q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if q.dtype == torch.float32:
+        if out_dtype not in (None, torch.float32):
+            raise ValueError("float32 inputs give float32 output")
+        fn, odt = "fa2_fwd_fp32", torch.float32
+    else:
+        odt = torch.bfloat16 if out_dtype is None else out_dtype
+        if odt == torch.bfloat16:
+            fn = "fa2_fwd"
+        elif odt == torch.float32:
+            fn = "fa2_fwd_o32"
+        else:
+            raise ValueError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    elif out.shape != q.shape or out.dtype != odt or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous %s tensor shaped like q" % odt)
+    if return_lse:
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        elif lse.shape != (B, H, N) or lse.dtype != torch.float32 \
+                or not lse.is_contiguous() or lse.device != q.device:
+            raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    else:
+        lse = None
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = getattr(lib(), fn)(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None,
+            B, H, N, d, ctypes.c_float(scale), int(bool(causal)), stream)
+    if rc != FA2_OK:
+        raise FA2Error(rc, fn)
+    return out, lse
+
+
+def raw_call(fn: str, q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, scale,
+             causal, stream=None) -> int:
+    """Call an entry point with raw integer pointers; returns the code."""
+    return int(getattr(lib(), fn)(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N,
+                                  d, ctypes.c_float(scale), int(causal), stream))

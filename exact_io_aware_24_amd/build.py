@@ -1,0 +1,68 @@
+"""Build the HIP library ``libfa2.so`` in-tree with hipcc for gfx950.
+
+    python -m exact_io_aware_24_amd.build
+
+Every translation unit is compiled for gfx950 only.  Packed fp32 VALU
+instructions are disabled (``-packed-fp32-ops``): hipcc would otherwise form
+them from plain float code, and this library does not rely on them.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libfa2.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+ARCH = "gfx950"
+
+SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_fp32.hip"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc",
+                 shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def compile_flags(extra=()) -> list:
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+            "-fvisibility=hidden", "-Wall", "-Wno-unused-result",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I" + INCLUDE, "-I" + CSRC] + list(extra)
+
+
+def build(verbose: bool = False, out: str = LIB_PATH, extra=()) -> str:
+    """Compile every source and link ``libfa2.so`` (always rebuilds)."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="fa2build") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
+            cmd = [cc] + compile_flags(extra) + lang + [
+                "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            objs.append(obj)
+        tmp_out = out + ".tmp%d" % os.getpid()
+        cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp_out
+               ] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp_out, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,134 @@
+// C-ABI entry points: argument validation (pure host code, before any HIP
+// call) and dispatch to the kernel launchers.  The declarations and the full
+// contract are in include/fa2.h.
+#include "fa2.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa2_internal.h"
+
+#define FA2_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range span(const void *p, int64_t bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool misaligned(const void *p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) != 0;
+}
+
+// Shared validation of every entry point.  in_bytes / out_bytes are the
+// element sizes of q/k/v and of o; rows_per_block is the kernel's query-block
+// height (bounds the grid size).
+int validate(const void *q, const void *k, const void *v, const void *o,
+             const float *lse, int B, int H, int N, int d, float scale,
+             int in_bytes, int out_bytes, int rows_per_block) {
+  if (!q || !k || !v || !o) return FA2_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return FA2_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
+  const int64_t bh = static_cast<int64_t>(B) * H;
+  const int64_t per_head = static_cast<int64_t>(N) * d;
+  const int64_t blocks = bh * ((static_cast<int64_t>(N) + rows_per_block - 1) /
+                               rows_per_block);
+  if (bh > INT32_MAX || per_head > INT32_MAX || blocks > INT32_MAX ||
+      bh * per_head > FA2_MAX_ELEMS)
+    return FA2_ERR_SHAPE;
+  if (!std::isfinite(scale)) return FA2_ERR_SCALE;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+      (lse && misaligned(lse)))
+    return FA2_ERR_ALIGN;
+  const int64_t elems = bh * per_head;
+  const Range rq = span(q, elems * in_bytes), rk = span(k, elems * in_bytes),
+              rv = span(v, elems * in_bytes), ro = span(o, elems * out_bytes);
+  if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv))
+    return FA2_ERR_ALIAS;
+  if (lse) {
+    const Range rl = span(lse, bh * N * static_cast<int64_t>(sizeof(float)));
+    if (overlaps(rl, rq) || overlaps(rl, rk) || overlaps(rl, rv) ||
+        overlaps(rl, ro))
+      return FA2_ERR_ALIAS;
+  }
+  return FA2_OK;
+}
+
+fa2::FwdArgs make_args(const void *q, const void *k, const void *v, void *o,
+                       float *lse, int B, int H, int N, int d, float scale,
+                       int causal) {
+  fa2::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = B * H;
+  a.n = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  return a;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? FA2_OK : FA2_ERR_HIP; }
+
+}  // namespace
+
+FA2_EXPORT int fa2_fwd(const void *q, const void *k, const void *v, void *o,
+                       float *lse, int B, int H, int N, int d, float scale,
+                       int causal, void *stream) {
+  int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2, 2,
+                    fa2::kBf16RowsPerBlock);
+  if (rc != FA2_OK) return rc;
+  return finish(fa2::launch_fwd_bf16(
+      make_args(q, k, v, o, lse, B, H, N, d, scale, causal), false,
+      static_cast<hipStream_t>(stream)));
+}
+
+FA2_EXPORT int fa2_fwd_o32(const void *q, const void *k, const void *v,
+                           float *o, float *lse, int B, int H, int N, int d,
+                           float scale, int causal, void *stream) {
+  int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2, 4,
+                    fa2::kBf16RowsPerBlock);
+  if (rc != FA2_OK) return rc;
+  return finish(fa2::launch_fwd_bf16(
+      make_args(q, k, v, o, lse, B, H, N, d, scale, causal), true,
+      static_cast<hipStream_t>(stream)));
+}
+
+FA2_EXPORT int fa2_fwd_fp32(const float *q, const float *k, const float *v,
+                            float *o, float *lse, int B, int H, int N, int d,
+                            float scale, int causal, void *stream) {
+  int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 4, 4,
+                    fa2::kFp32RowsPerBlock);
+  if (rc != FA2_OK) return rc;
+  return finish(fa2::launch_fwd_fp32(
+      make_args(q, k, v, o, lse, B, H, N, d, scale, causal),
+      static_cast<hipStream_t>(stream)));
+}
+
+FA2_EXPORT const char *fa2_strerror(int code) {
+  switch (code) {
+    case FA2_OK: return "success";
+    case FA2_ERR_NULL: return "a required pointer (q, k, v or o) is NULL";
+    case FA2_ERR_SHAPE:
+      return "invalid shape: B, H and N must be >= 1 and the tensors within "
+             "the supported size";
+    case FA2_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
+    case FA2_ERR_SCALE: return "scale is not finite";
+    case FA2_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FA2_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA2_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown fa2 error code";
+  }
+}
+
+FA2_EXPORT int fa2_version(void) { return 1; }

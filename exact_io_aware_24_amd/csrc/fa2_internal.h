@@ -1,0 +1,33 @@
+// Internal launch interface between the C-ABI layer (fa2_api.cpp) and the
+// kernel translation units.  Not installed, not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa2 {
+
+// Arguments shared by every forward kernel.  All pointers are device
+// pointers; shapes have been validated by the caller.
+struct FwdArgs {
+  const void *q, *k, *v;  // [B*H][N][d]
+  void *o;                // [B*H][N][d]
+  float *lse;             // [B*H][N] or nullptr
+  int bh;                 // B*H
+  int n;                  // sequence length
+  int d;                  // head dimension (64 or 128)
+  float scale;            // multiplies q.k
+  bool causal;
+};
+
+// bf16 q/k/v on MFMA; o is bf16 (o32 == false) or fp32 (o32 == true).
+hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s);
+
+// fp32 q/k/v/o, fp32 arithmetic throughout.
+hipError_t launch_fwd_fp32(const FwdArgs &a, hipStream_t s);
+
+// Query rows per workgroup of each kernel (the grid is B*H*ceil(N/rows)).
+constexpr int kBf16RowsPerBlock = 128;
+constexpr int kFp32RowsPerBlock = 64;
+
+}  // namespace fa2

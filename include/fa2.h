@@ -1,0 +1,118 @@
+/*
+ * fa2.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * Operation (all entry points):
+ *
+ *     O[b,h] = softmax(scale * Q[b,h] K[b,h]^T + M) V[b,h]
+ *     lse[b,h,i] = ln( sum_{j visible to i} exp(scale * q_i . k_j) )
+ *
+ * for every batch index b < B and head h < H independently.  M is 0, or,
+ * when `causal` is non-zero, -inf where key j > query i (autoregressive mask
+ * aligned at the top-left corner: query i sees keys 0..i).
+ *
+ * This is the exact attention of the FlashAttention pages: the definition of
+ * standard attention (the shakilmahmud.com page "Large language models part
+ * 06: FlashAttention -- GPU SRAM, tiling, online softmax", section 1, and the
+ * standard-attention recap of the unite.ai page "Flash Attention:
+ * revolutionising transformer efficiency") evaluated tile by tile with the
+ * online-softmax merge of section 2 of the same shakilmahmud.com page, in the
+ * FlashAttention-2 order (outer loop over query blocks, inner loop over K/V
+ * blocks, the final division by the softmax denominator deferred until the
+ * inner loop ends -- section 1 of the itimpress.au page "FlashAttention
+ * scaling, multi-GPU training and weight quantisation"; the parallelism over
+ * query blocks is improvement 2 of the "FlashAttention-2 (BN)" systems-
+ * analysis wiki article).  The N x N score matrix is never written to memory.
+ * The pages define no log-sum-exp output and no mask; both readings above are
+ * this library's.
+ *
+ * Layout: q, k, v, o are contiguous row-major [B][H][N][d] device arrays
+ * (element (b,h,i,c) at ((b*H + h)*N + i)*d + c); lse is a contiguous
+ * [B][H][N] float32 device array.
+ *
+ * Ownership and lifetime: the caller allocates and owns every buffer; the
+ * library allocates no device or host memory and keeps no state other than
+ * what the HIP runtime caches.  All pointers are device pointers (hipMalloc
+ * or equivalent) of the current HIP device.  Calls are thread-safe.
+ *
+ * Asynchrony: every entry point enqueues its kernel on `stream` (a
+ * hipStream_t; NULL means the null stream) and returns without waiting.
+ * Inputs must stay valid and unmodified, and outputs must not be read, until
+ * the stream reaches that point.  Results are deterministic: the same inputs
+ * give bit-identical outputs on every call (no atomics, fixed reduction
+ * order).
+ *
+ * Aliasing: q, k and v may alias one another (they are only read).  o and
+ * lse must not overlap any input or each other (FA2_ERR_ALIAS).
+ *
+ * Errors: every argument is validated on the host before any HIP call, so a
+ * rejected call has no effect and enqueues nothing.  A non-zero return is
+ * one of the FA2_ERR_* codes below; fa2_strerror() names it.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA2_OK 0
+#define FA2_ERR_NULL (-1)    /* q, k, v or o is NULL                           */
+#define FA2_ERR_SHAPE (-2)   /* B, H or N < 1, or a size limit below exceeded */
+#define FA2_ERR_HEADDIM (-3) /* d is not 64 or 128                             */
+#define FA2_ERR_SCALE (-4)   /* scale is NaN or infinite                       */
+#define FA2_ERR_ALIGN (-5)   /* a pointer is not 16-byte aligned               */
+#define FA2_ERR_ALIAS (-6)   /* o or lse overlaps an input or each other       */
+#define FA2_ERR_HIP (-7)     /* the kernel launch failed (hipGetLastError)     */
+
+/* Size limits (FA2_ERR_SHAPE beyond them): B*H*N*d <= FA2_MAX_ELEMS elements
+   per tensor (2^40, far above one GPU's memory); N*d, B*H and the number of
+   workgroups (B*H*ceil(N/128), or ceil(N/64) for fa2_fwd_fp32) each
+   <= 2^31 - 1, because per-head offsets and grid indices are 32-bit. */
+#define FA2_MAX_ELEMS (1LL << 40)
+
+/*
+ * fa2_fwd -- bf16 inputs, bf16 output.
+ *   q, k, v : const bf16 [B][H][N][d]  (bfloat16 bit patterns, 2 bytes each)
+ *   o       : bf16 [B][H][N][d], written, round-to-nearest-even from fp32
+ *   lse     : float [B][H][N] or NULL (then no log-sum-exp is written)
+ *   B, H, N : batch, heads, sequence length (queries and keys), each >= 1
+ *   d       : head dimension, 64 or 128
+ *   scale   : multiplies q.k before the softmax (usually 1/sqrt(d)); any
+ *             finite value, including 0 and negative values
+ *   causal  : 0 = no mask, non-zero = query i sees keys j <= i
+ *   stream  : hipStream_t to enqueue on (NULL = null stream)
+ * Products of bf16 values are exact in fp32; S and the running statistics
+ * are fp32, probabilities are rounded to bf16 for the P.V product, whose
+ * accumulation is fp32.
+ */
+int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+            int B, int H, int N, int d, float scale, int causal, void *stream);
+
+/*
+ * fa2_fwd_o32 -- as fa2_fwd, but o is float [B][H][N][d]: the same kernel
+ * with the final fp32 result stored without the last bf16 rounding.
+ */
+int fa2_fwd_o32(const void *q, const void *k, const void *v, float *o,
+                float *lse, int B, int H, int N, int d, float scale,
+                int causal, void *stream);
+
+/*
+ * fa2_fwd_fp32 -- float32 q, k, v and o; every step (scores, softmax,
+ * probabilities, P.V) in fp32 arithmetic, for exactness checks on small
+ * problems.  Same shapes, mask, scale, lse, alignment and error rules.
+ */
+int fa2_fwd_fp32(const float *q, const float *k, const float *v, float *o,
+                 float *lse, int B, int H, int N, int d, float scale,
+                 int causal, void *stream);
+
+/* Static English description of a return code (never NULL). */
+const char *fa2_strerror(int code);
+
+/* Library ABI version: 1. */
+int fa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

@@ -1,0 +1,131 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, it
+exports every symbol include/fa2.h declares, and every argument error is
+reported before any HIP call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_io_aware_24_amd as fa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa2_\w+)\s*\(", txt)))
+
+
+def header_codes():
+    return {m.group(1): int(m.group(2)) for m in re.finditer(
+        r"#define\s+(FA2_(?:OK|ERR_\w+))\s+\(?(-?\d+)\)?", open(HEADER).read())}
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa2.LIB_PATH):
+        pytest.fail("libfa2.so not built (python -m exact_io_aware_24_amd.build)")
+    return fa2.lib()
+
+
+def test_exports_match_header(L):
+    declared = header_functions()
+    assert declared == sorted(fa2.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", fa2.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted(set(re.findall(r"\bT\s+(fa2_\w+)$", out, flags=re.M)))
+    assert exported == declared
+    for name in declared:
+        assert getattr(L, name) is not None
+
+
+def test_codes_match_header():
+    codes = header_codes()
+    for name, val in codes.items():
+        assert getattr(fa2, name) == val, name
+
+
+def test_version_and_strerror(L):
+    assert fa2.version() == 1
+    seen = set()
+    for name, code in header_codes().items():
+        msg = fa2.strerror(code)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert "unknown" in fa2.strerror(12345)
+
+
+# Fake, never-dereferenced device addresses: every call below is rejected by
+# validation before the library makes any HIP call.
+MiB = 1 << 20
+Q, K, V, O, LSE = (0x10000000 + i * 64 * MiB for i in range(5))
+FUNCS = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_fp32")
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=LSE, B=1, H=2, N=64, d=64, scale=0.125,
+            causal=0)
+
+
+def call(fn, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa2.raw_call(fn, a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                        a["H"], a["N"], a["d"], a["scale"], a["causal"])
+
+
+@pytest.mark.parametrize("fn", FUNCS)
+def test_null_pointers(L, fn):
+    for key in ("q", "k", "v", "o"):
+        assert call(fn, **{key: None}) == fa2.FA2_ERR_NULL
+
+
+@pytest.mark.parametrize("fn", FUNCS)
+def test_bad_shapes(L, fn):
+    for kw in (dict(B=0), dict(H=0), dict(N=0), dict(B=-1), dict(N=-5),
+               dict(N=1 << 30, d=128),              # N*d over 2^31-1
+               dict(B=1 << 16, H=1 << 16, N=1)):     # B*H over 2^31-1
+        assert call(fn, **kw) == fa2.FA2_ERR_SHAPE, kw
+
+
+@pytest.mark.parametrize("fn", FUNCS)
+def test_bad_head_dim(L, fn):
+    for d in (0, 1, 32, 63, 96, 127, 256):
+        assert call(fn, d=d) == fa2.FA2_ERR_HEADDIM, d
+
+
+@pytest.mark.parametrize("fn", FUNCS)
+def test_bad_scale(L, fn):
+    for s in (float("nan"), float("inf"), float("-inf")):
+        assert call(fn, scale=s) == fa2.FA2_ERR_SCALE
+
+
+@pytest.mark.parametrize("fn", FUNCS)
+def test_misaligned(L, fn):
+    for key in ("q", "k", "v", "o", "lse"):
+        assert call(fn, **{key: GOOD[key] + 8}) == fa2.FA2_ERR_ALIGN, key
+
+
+@pytest.mark.parametrize("fn", FUNCS)
+def test_aliasing(L, fn):
+    assert call(fn, o=Q) == fa2.FA2_ERR_ALIAS
+    assert call(fn, o=V + 4096) == fa2.FA2_ERR_ALIAS
+    assert call(fn, lse=K) == fa2.FA2_ERR_ALIAS
+    assert call(fn, lse=O + 16) == fa2.FA2_ERR_ALIAS
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa2.forward(q, q, q)
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa2.forward(q[0], q[0], q[0])
+    with pytest.raises(TypeError):
+        fa2.forward(None, q, q)
