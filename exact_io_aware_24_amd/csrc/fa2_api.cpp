@@ -29,10 +29,13 @@ bool misaligned(const void *p) {
 
 // Shared validation of every entry point.  in_bytes / out_bytes are the
 // element sizes of q/k/v and of o; rows_per_block is the kernel's query-block
-// height (bounds the grid size).
+// height (bounds the grid size); max_per_head bounds N*d (the bf16 kernel
+// addresses one head with 32-bit byte offsets, including one tile of reads
+// past the end that the hardware bounds check turns into zeros).
 int validate(const void *q, const void *k, const void *v, const void *o,
              const float *lse, int B, int H, int N, int d, float scale,
-             int in_bytes, int out_bytes, int rows_per_block) {
+             int in_bytes, int out_bytes, int rows_per_block,
+             int64_t max_per_head) {
   if (!q || !k || !v || !o) return FA2_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return FA2_ERR_SHAPE;
   if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
@@ -40,7 +43,7 @@ int validate(const void *q, const void *k, const void *v, const void *o,
   const int64_t per_head = static_cast<int64_t>(N) * d;
   const int64_t blocks = bh * ((static_cast<int64_t>(N) + rows_per_block - 1) /
                                rows_per_block);
-  if (bh > INT32_MAX || per_head > INT32_MAX || blocks > INT32_MAX ||
+  if (bh > INT32_MAX || per_head > max_per_head || blocks > INT32_MAX ||
       bh * per_head > FA2_MAX_ELEMS)
     return FA2_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA2_ERR_SCALE;
@@ -86,7 +89,7 @@ FA2_EXPORT int fa2_fwd(const void *q, const void *k, const void *v, void *o,
                        float *lse, int B, int H, int N, int d, float scale,
                        int causal, void *stream) {
   int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2, 2,
-                    fa2::kBf16RowsPerBlock);
+                    fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
       make_args(q, k, v, o, lse, B, H, N, d, scale, causal), false,
@@ -97,7 +100,7 @@ FA2_EXPORT int fa2_fwd_o32(const void *q, const void *k, const void *v,
                            float *o, float *lse, int B, int H, int N, int d,
                            float scale, int causal, void *stream) {
   int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2, 4,
-                    fa2::kBf16RowsPerBlock);
+                    fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
       make_args(q, k, v, o, lse, B, H, N, d, scale, causal), true,
@@ -108,7 +111,7 @@ FA2_EXPORT int fa2_fwd_fp32(const float *q, const float *k, const float *v,
                             float *o, float *lse, int B, int H, int N, int d,
                             float scale, int causal, void *stream) {
   int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 4, 4,
-                    fa2::kFp32RowsPerBlock);
+                    fa2::kFp32RowsPerBlock, INT32_MAX);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_fp32(
       make_args(q, k, v, o, lse, B, H, N, d, scale, causal),

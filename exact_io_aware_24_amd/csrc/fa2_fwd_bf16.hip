@@ -6,10 +6,12 @@
 //   "FlashAttention scaling, multi-GPU training and weight quantisation",
 //   section 1):
 //     S  = K_tile . Q_block^T            bf16 MFMA, fp32 accumulate
-//     m' = max(m, rowmax(S) * c)          c = scale * log2(e)   (base-2 units)
-//     P~ = 2^(S*c - m')                   fp32, hardware exp2
-//     l  = l * 2^(m - m') + rowsum(P~)
-//     O~ = O~ * 2^(m - m') + P~ . V_tile  P~ rounded to bf16, MFMA, fp32 acc
+//     mt = rowmax(S) * c                  c = scale * log2(e)   (base-2 units)
+//     if mt > m + 8 for any row of the wave:   (lazy rescale, see below)
+//         a = 2^(m - max(m, mt)); m = max(m, mt); l *= a; O~ *= a
+//     P~ = 2^(S*c - m)                    fp32, hardware exp2
+//     l  = l + rowsum(P~)
+//     O~ = O~ + P~ . V_tile               P~ rounded to bf16, MFMA, fp32 acc
 //   and after the last tile O = O~ / l, lse = (m + log2 l) * ln 2.
 // The running (m, l, O~) update is the two-block online-softmax merge of the
 // shakilmahmud.com page "Large language models part 06: FlashAttention --
@@ -18,6 +20,12 @@
 // reduction of non-matmul work, the same itimpress.au section).  One
 // workgroup per (batch*head, query block) spreads one head over many compute
 // units (improvement 2 of the "FlashAttention-2 (BN)" wiki article).
+//
+// Lazy rescale: the merge is exact for ANY common reference value m, not only
+// the true running maximum, as long as the same m is used for l and O~.  The
+// reference is therefore raised only when a tile's maximum exceeds it by more
+// than 8 (a factor 256), which keeps every P~ <= 2^8 (no overflow, the same
+// relative bf16 precision) and skips the O~ rescale on most tiles.
 //
 // gfx950 mapping (this library's design, not the pages'):
 //  * 256 threads = 4 wave64s; wave w owns query rows [32w, 32w+32) of the
@@ -36,18 +44,24 @@
 //    O^T += V^T P^T, and V^T is read with one 16-byte LDS load per operand.
 //  * K is staged row-major and V transposed (V^T, keys contiguous) in LDS,
 //    both with XOR swizzles of their 16-byte chunks so that every 8-lane
-//    phase of a 128-bit LDS access touches 32 distinct banks.  The next tile
-//    is fetched from HBM into registers while the current one is consumed;
-//    LDS is double-buffered, one barrier per tile.
-//  * Causal: tiles past a wave's last query are skipped (the wave only
-//    helps to stage them); the mask is applied only in tiles that cross the
-//    diagonal or the ragged end of the sequence.  Query blocks are issued
-//    longest first.
+//    phase of a 128-bit LDS access touches 32 distinct banks.  Swizzles use
+//    only lane bits that leave compile-time parts of the address additive,
+//    so almost every LDS access is a per-lane base plus an immediate.
+//  * Global loads are raw buffer loads with the per-head extent as the
+//    buffer size: rows past the end of the sequence read as zero in hardware,
+//    with no branches.  The next tile is fetched into registers while the
+//    current one is consumed; LDS is double-buffered, one barrier per tile.
+//  * Causal: tiles past a wave's last query are skipped by that wave (it only
+//    helps to stage them); the mask is applied only in the tiles that cross
+//    the diagonal or the ragged end of the sequence, which run in a separate
+//    loop after the unmasked ones.  Query blocks are issued longest first.
 //  * Workgroup ids are remapped so that the blocks of one head run on the
 //    same XCD (hardware deals workgroups round-robin over the 8 XCDs), which
 //    keeps that head's K/V in one L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fa2_internal.h"
 
@@ -56,14 +70,17 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kRows = kBf16RowsPerBlock;  // 128 query rows per workgroup
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kLog2e = 1.442695040888963407360f;
+constexpr float kRescaleThreshold = 8.0f;  // base-2 units: P~ <= 256
+// Buffer descriptor word 3: 32-bit data format, raw (untyped) addressing.
+constexpr int kBufWord3 = 0x00020000;
 
 struct Params {
   const uint16_t *q, *k, *v;
@@ -75,11 +92,20 @@ struct Params {
   float c;        // scale * log2(e)
 };
 
-// Keys per K/V tile: 64 at d = 128, 128 at d = 64 (16 KB of K and 16 KB of V
-// either way, 32 MFMA per wave per tile).
 template <int D>
-struct TileCfg {
-  static constexpr int BC = (D == 128) ? 64 : 128;
+struct Cfg {
+  static constexpr int BC = (D == 128) ? 64 : 128;  // keys per tile
+  static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  static constexpr int NKT = BC / 32;               // 32-key sub-tiles
+  static constexpr int NDT = D / 16;                // 16-dim MFMA k-steps
+  static constexpr int NCT = D / 32;                // 32-wide O^T row tiles
+  static constexpr int KLOADS = BC * KCH / kThreads;
+  static constexpr int VCOLS = D / 4;               // 4-column V groups
+  static constexpr int TILE = BC * D;               // elements per K or V tile
+  static constexpr int TILE_BYTES = TILE * 2;       // 16 KB either way
+  static_assert(KLOADS * kThreads == BC * KCH, "K tile split");
+  static_assert((BC / 8) * VCOLS == kThreads, "V tile split");
+  static_assert(kThreads / KCH * D * 2 == 4096, "K load stride");
 };
 
 // Row permutation inside each 16-row group: swap bits 2 and 3.
@@ -87,11 +113,11 @@ __device__ __forceinline__ int perm16(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// Swizzle of V^T rows: 16-byte chunk j of row c lives at chunk j ^ vsw(c).
-__device__ __forceinline__ int vsw(int c) { return (c ^ (c >> 3)) & 7; }
+// Swizzle of V^T rows (columns of V): 16-byte chunk j of row c is stored at
+// chunk j ^ vsw(c).  It uses bits 0-4 of c only, so rows 32 apart share it.
+__device__ __forceinline__ int vsw(int c) { return (c & 7) ^ ((c >> 3) & 3); }
 
-// Both half-waves combined: returns (x of lanes 0-31, x of lanes 32-63) as
-// seen from every lane.
+// (x of lanes 0-31, x of lanes 32-63) as seen from every lane.
 __device__ __forceinline__ void halves(float x, float &lo, float &hi) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
                                             __float_as_uint(x), false, false);
@@ -103,21 +129,176 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
+template <typename T>
+__device__ __forceinline__ T lds_load(const char *base, int byte_off) {
+  return *reinterpret_cast<const T *>(base + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store(char *base, int byte_off, T v) {
+  *reinterpret_cast<T *>(base + byte_off) = v;
+}
+
+// Everything one wave needs while it walks the K/V tiles.
+template <int D>
+struct WaveState {
+  bf16x8 qreg[Cfg<D>::NDT];
+  f32x16 oacc[Cfg<D>::NCT];
+  float m_run;  // reference max (base-2 scaled units)
+  float l_run;  // this half-wave's share of the running sum
+};
+
+// Per-thread byte offsets that stay fixed for the whole kernel.
+template <int D>
+struct Offsets {
+  int k_rd[4];  // K operand reads, 16-dim steps 0..3 (steps 4..7 at +128 B)
+  int v_rd[4];  // V^T operand reads, (sub-tile parity, 16-key half) 0..3
+  int k_wr;     // K staging write (loads it = 0..3 at +4096 B each)
+  int v_wr[4];  // V^T staging writes, columns 4*vcc + e
+  int k_ld;     // K buffer-load offset within a tile
+  int v_ld;     // V buffer-load offset within a tile (rows r at +r*D*2)
+};
+
+template <int D>
+__device__ __forceinline__ void gload(const __amdgpu_buffer_rsrc_t &rk,
+                                      const __amdgpu_buffer_rsrc_t &rv,
+                                      const Offsets<D> &off, int tile_byte,
+                                      u32x4 (&kpre)[Cfg<D>::KLOADS],
+                                      u32x2 (&vpre)[8]) {
+#pragma unroll
+  for (int it = 0; it < Cfg<D>::KLOADS; ++it)
+    kpre[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k_ld,
+                                                     tile_byte + it * 4096, 0);
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    vpre[r] = __builtin_amdgcn_raw_buffer_load_b64(rv, off.v_ld + r * D * 2,
+                                                   tile_byte, 0);
+}
+
+template <int D, int BUF>
+__device__ __forceinline__ void swrite(char *smem, const Offsets<D> &off,
+                                       const u32x4 (&kpre)[Cfg<D>::KLOADS],
+                                       const u32x2 (&vpre)[8]) {
+  using C = Cfg<D>;
+  char *kb = smem + BUF * C::TILE_BYTES;
+  char *vb = smem + (2 + BUF) * C::TILE_BYTES;
+#pragma unroll
+  for (int it = 0; it < C::KLOADS; ++it) lds_store(kb, off.k_wr + it * 4096, kpre[it]);
+  // 8 keys x 4 columns -> 4 columns x 8 keys (bf16 transpose in registers)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    u32x4 outv;
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const uint32_t a = (e < 2) ? vpre[2 * pr].x : vpre[2 * pr].y;
+      const uint32_t b = (e < 2) ? vpre[2 * pr + 1].x : vpre[2 * pr + 1].y;
+      outv[pr] = (e & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
+                         : __builtin_amdgcn_perm(b, a, 0x05040100u);
+    }
+    lds_store(vb, off.v_wr[e], outv);
+  }
+}
+
+// One K/V tile for one wave.  MASKED tiles apply the causal / sequence-end
+// mask; unmasked tiles need no compare at all.
+template <int D, bool CAUSAL, bool MASKED, int BUF>
+__device__ __forceinline__ void tile(const char *smem, const Offsets<D> &off,
+                                     WaveState<D> &st, float c, int j0, int N,
+                                     int qi, int hh) {
+  using C = Cfg<D>;
+  const char *kb = smem + BUF * C::TILE_BYTES;
+  const char *vb = smem + (2 + BUF) * C::TILE_BYTES;
+
+  // -- S^T = K Q^T ---------------------------------------------------------
+  f32x16 s[C::NKT];
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+    // operands in groups of four: 16 registers in flight, not 32
+#pragma unroll
+    for (int g = 0; g < C::NDT; g += 4) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = lds_load<bf16x8>(kb, off.k_rd[i] + (g >> 2) * 128 + kt * 32 * D * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], st.qreg[g + i],
+                                                        s[kt], 0, 0, 0);
+    }
+  }
+
+  // -- mask: register r of sub-tile kt holds key j0 + 32kt + 16(r/8) + 8hh + r%8
+  if (MASKED) {
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * kt + 16 * (r >> 3) + 8 * hh + (r & 7);
+        if (key >= N || (CAUSAL && key > qi)) s[kt][r] = -INFINITY;
+      }
+  }
+
+  // -- online softmax --------------------------------------------------------
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  float mlo, mhi;
+  halves(mx, mlo, mhi);
+  mx = fmaxf(mlo, mhi);
+  const float m_tile = (MASKED && mx == -INFINITY) ? -INFINITY : mx * c;
+  if (__builtin_amdgcn_ballot_w64(m_tile > st.m_run + kRescaleThreshold)) {
+    const float m_new = fmaxf(st.m_run, m_tile);
+    const float alpha =
+        (m_new == -INFINITY) ? 1.f : fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[ct][r] *= alpha;
+  }
+  const float mu = (MASKED && st.m_run == -INFINITY) ? 0.f : st.m_run;
+
+  bf16x8 pb[C::NKT][2];
+  float rs = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float sv = s[kt][8 * u + e];
+        float x = fast_exp2(__builtin_fmaf(sv, c, -mu));
+        if (MASKED) x = (sv == -INFINITY) ? 0.f : x;
+        rs += x;
+        pb[kt][u][e] = static_cast<__bf16>(x);
+      }
+  st.l_run += rs;
+
+  // -- O^T += V^T P^T ----------------------------------------------------------
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 a[C::NCT];
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct)
+        a[ct] = lds_load<bf16x8>(vb, off.v_rd[(kt & 1) * 2 + u] + (kt >> 1) * 128 +
+                                         ct * 32 * C::BC * 2);
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct)
+        st.oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ct], pb[kt][u],
+                                                              st.oacc[ct], 0, 0, 0);
+    }
+}
+
 template <int D, bool CAUSAL, bool O32>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
-  constexpr int BC = TileCfg<D>::BC;
-  constexpr int KCH = D / 8;                        // 16-byte chunks per K row
-  constexpr int KMASK = (KCH < 16 ? KCH : 16) - 1;  // K swizzle width
-  constexpr int NKT = BC / 32;                      // 32-key sub-tiles
-  constexpr int NDT = D / 16;                       // 16-dim MFMA k-steps
-  constexpr int NCT = D / 32;                       // 32-wide O^T row tiles
-  constexpr int KLOADS = BC * KCH / kThreads;       // 16-byte K chunks/thread
-  constexpr int VCOLS = D / 4;                      // 4-column V groups
-  static_assert(KLOADS * kThreads == BC * KCH, "K tile split");
-  static_assert((BC / 8) * VCOLS == kThreads, "V tile split");
-
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * BC];
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[4 * C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int lr = lane & 31;  // query column of this lane in S^T / O^T
   const int hh = lane >> 5;  // half-wave
 
-  // ---- workgroup -> (head, query block) --------------------------------
+  // ---- workgroup -> (head, query block) ----------------------------------
   const int w = blockIdx.x;
   const int per_xcd = p.total >> 3;
   int logical = w;
@@ -136,221 +317,137 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
 
   const int N = p.n;
   const size_t head = static_cast<size_t>(bh) * N * D;
-  const uint16_t *__restrict__ qh = p.q + head;
-  const uint16_t *__restrict__ kh = p.k + head;
-  const uint16_t *__restrict__ vh = p.v + head;
+  const int head_bytes = N * D * 2;  // < 2^32 - 2^17 (host-validated)
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(p.q + head), 0, head_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(p.k + head), 0, head_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(p.v + head), 0, head_bytes, kBufWord3);
+
   const int q0 = qb * kRows;      // first query of the block
   const int qw = q0 + wv * 32;    // first query of this wave
   const int qi = qw + lr;         // this lane's query
 
-  // ---- Q into registers (B operand of S^T = K Q^T) ---------------------
+  // ---- fixed offsets -------------------------------------------------------
+  Offsets<D> off;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    off.k_rd[i] = (perm16(lr) * D + (((2 * i + hh) ^ (lr & 7)) * 8)) * 2;
+    const int chunk = 2 * i + hh;  // (sub-tile parity, half) -> 16-B chunk
+    off.v_rd[i] = (lr * C::BC + ((chunk ^ vsw(lr)) * 8)) * 2;
+  }
+  {
+    const int row = tid / C::KCH, ch = tid % C::KCH;
+    off.k_wr = (row * D + ((ch ^ (perm16(row) & 7)) * 8)) * 2;
+    off.k_ld = (row * D + ch * 8) * 2;
+    const int vcc = tid % C::VCOLS, vjg = tid / C::VCOLS;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int col = vcc * 4 + e;
+      off.v_wr[e] = (col * C::BC + ((vjg ^ vsw(col)) * 8)) * 2;
+    }
+    off.v_ld = ((vjg * 8) * D + vcc * 4) * 2;
+  }
+
+  // ---- Q into registers (B operand of S^T = K Q^T) -------------------------
+  WaveState<D> st;
   float c = p.c;
   uint32_t qflip = 0;
   if (c < 0.f) {  // exact: negate q (bf16 sign bit) and use -c
     c = -c;
     qflip = 0x80008000u;
   }
-  bf16x8 qreg[NDT];
+  const int q_ld = (qi * D + 8 * hh) * 2;
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < N) {
-      x = *reinterpret_cast<const u32x4 *>(qh + static_cast<size_t>(qi) * D +
-                                            16 * t + 8 * hh);
-      x ^= qflip;
-    }
-    qreg[t] = __builtin_bit_cast(bf16x8, x);
+  for (int t = 0; t < C::NDT; ++t) {
+    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, q_ld + 32 * t, 0, 0);
+    x ^= qflip;
+    st.qreg[t] = __builtin_bit_cast(bf16x8, x);
   }
+#pragma unroll
+  for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.oacc[ct][r] = 0.f;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
 
-  // ---- tile staging ----------------------------------------------------
+  // ---- tile schedule -------------------------------------------------------
+  // Tiles [0, n_full) need no mask for any row of the block; the rest (the
+  // diagonal band when causal, the ragged end of the sequence) are masked.
   const int kend = CAUSAL ? min(N, q0 + kRows) : N;
-  const int ntiles = (kend + BC - 1) / BC;
+  const int ntiles = (kend + C::BC - 1) / C::BC;
+  int n_full = CAUSAL ? (q0 + 1) / C::BC : N / C::BC;
+  if (n_full > ntiles) n_full = ntiles;
+  if (n_full * C::BC > N) n_full = N / C::BC;
 
-  u32x4 kpre[KLOADS];
+  u32x4 kpre[C::KLOADS];
   u32x2 vpre[8];
-  const int vcc = tid % VCOLS;  // this thread's 4-column group of V
-  const int vjg = tid / VCOLS;  // and its 8-key group
-
-  auto gload = [&](int j0) {
-#pragma unroll
-    for (int it = 0; it < KLOADS; ++it) {
-      const int id = tid + kThreads * it;
-      const int row = id / KCH, ch = id % KCH;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (j0 + row < N)
-        x = *reinterpret_cast<const u32x4 *>(
-            kh + static_cast<size_t>(j0 + row) * D + ch * 8);
-      kpre[it] = x;
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = j0 + vjg * 8 + r;
-      u32x2 x = {0u, 0u};
-      if (row < N)
-        x = *reinterpret_cast<const u32x2 *>(vh + static_cast<size_t>(row) * D +
-                                              vcc * 4);
-      vpre[r] = x;
-    }
-  };
-
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < KLOADS; ++it) {
-      const int id = tid + kThreads * it;
-      const int row = id / KCH, ch = id % KCH;
-      const int pos = ch ^ (perm16(row) & KMASK);
-      *reinterpret_cast<u32x4 *>(&Ks[buf][row * D + pos * 8]) = kpre[it];
-    }
-    // 8 keys x 4 columns -> 4 columns x 8 keys (bf16 transpose in registers)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u32x4 outv;
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const uint32_t a = (e < 2) ? vpre[2 * pr].x : vpre[2 * pr].y;
-        const uint32_t b = (e < 2) ? vpre[2 * pr + 1].x : vpre[2 * pr + 1].y;
-        outv[pr] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u))
-                           : ((a & 0xffffu) | (b << 16));
-      }
-      const int col = vcc * 4 + e;
-      const int pos = vjg ^ vsw(col);
-      *reinterpret_cast<u32x4 *>(&Vs[buf][col * BC + pos * 8]) = outv;
-    }
-  };
-
-  gload(0);
-  swrite(0);
+  gload<D>(rk, rv, off, 0, kpre, vpre);
+  swrite<D, 0>(smem, off, kpre, vpre);
   __syncthreads();
 
-  f32x16 oacc[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[ct][r] = 0.f;
-  float m_run = -INFINITY;  // running max, base-2 scaled units
-  float l_run = 0.f;        // this half-wave's share of the running sum
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * BC;
-    const int buf = t & 1;
+  auto step = [&](auto buf_tag, auto masked_tag, int t) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int j0 = t * C::BC;
     const bool more = t + 1 < ntiles;
-    if (more) gload(j0 + BC);
-
-    const bool active = !CAUSAL || j0 <= qw + 31;
-    if (active) {
-      // -- S^T = K Q^T ---------------------------------------------------
-      f32x16 s[NKT];
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-        const uint16_t *krow = &Ks[buf][(32 * kt + perm16(lr)) * D];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int pos = (2 * dt + hh) ^ (lr & KMASK);
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + pos * 8);
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dt], s[kt],
-                                                          0, 0, 0);
-        }
-      }
-      // -- mask (diagonal / ragged tiles only) ---------------------------
-      // register r of sub-tile kt holds key j0 + 32kt + 16(r/8) + 8hh + r%8
-      const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw);
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * kt + 16 * (r >> 3) + 8 * hh + (r & 7);
-            if (key >= N || (CAUSAL && key > qi)) s[kt][r] = -INFINITY;
-          }
-      }
-      // -- online softmax --------------------------------------------------
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      float mlo, mhi;
-      halves(mx, mlo, mhi);
-      mx = fmaxf(mlo, mhi);
-      const float m_tile = (mx == -INFINITY) ? -INFINITY : mx * c;
-      const float m_new = fmaxf(m_run, m_tile);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-
-      bf16x8 pb[NKT][2];
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float sv = s[kt][8 * u + e];
-            float x = fast_exp2(__builtin_fmaf(sv, c, -m_use));
-            if (need_mask) x = (sv == -INFINITY) ? 0.f : x;
-            rs += x;
-            pb[kt][u][e] = static_cast<__bf16>(x);
-          }
-        }
-      l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[ct][r] *= alpha;
-
-      // -- O^T += V^T P^T --------------------------------------------------
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int chunk = 4 * kt + 2 * u + hh;
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            const int col = 32 * ct + lr;
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                &Vs[buf][col * BC + (chunk ^ vsw(col)) * 8]);
-            oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                a, pb[kt][u], oacc[ct], 0, 0, 0);
-          }
-        }
-    }
-
-    if (more) swrite(buf ^ 1);
+    if (more) gload<D>(rk, rv, off, (j0 + C::BC) * D * 2, kpre, vpre);
+    if (!MASKED || !CAUSAL || j0 <= qw + 31)
+      tile<D, CAUSAL, MASKED, BUF>(smem, off, st, c, j0, N, qi, hh);
+    if (more) swrite<D, 1 - BUF>(smem, off, kpre, vpre);
     __syncthreads();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using Unmasked = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+
+  int t = 0;
+  for (; t + 2 <= n_full; t += 2) {
+    step(B0{}, Unmasked{}, t);
+    step(B1{}, Unmasked{}, t + 1);
+  }
+  if (t < n_full) {
+    step(B0{}, Unmasked{}, t);
+    ++t;
+  }
+  for (; t < ntiles; ++t) {
+    if (t & 1)
+      step(B1{}, Masked{}, t);
+    else
+      step(B0{}, Masked{}, t);
   }
 
-  // ---- epilogue: O = O~ / l, lse ----------------------------------------
+  // ---- epilogue: O = O~ / l, lse ---------------------------------------------
   float llo, lhi;
-  halves(l_run, llo, lhi);
+  halves(st.l_run, llo, lhi);
   const float l_tot = llo + lhi;
   const float inv = 1.0f / l_tot;
   if (qi < N) {
     // O^T register r of row tile ct holds column 32ct + 8(r/4) + 4hh + r%4
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int col = 32 * ct + 8 * a + 4 * hh;
-        const size_t off = static_cast<size_t>(qi) * D + col;
+        const size_t o_off = head + static_cast<size_t>(qi) * D + col;
         if (O32) {
           f32x4 ov;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) ov[b] = oacc[ct][4 * a + b] * inv;
-          *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + head + off) = ov;
+          for (int b = 0; b < 4; ++b) ov[b] = st.oacc[ct][4 * a + b] * inv;
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + o_off) = ov;
         } else {
           __bf16 ob[4];
 #pragma unroll
           for (int b = 0; b < 4; ++b)
-            ob[b] = static_cast<__bf16>(oacc[ct][4 * a + b] * inv);
-          *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p.o) + head + off) =
+            ob[b] = static_cast<__bf16>(st.oacc[ct][4 * a + b] * inv);
+          *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p.o) + o_off) =
               __builtin_bit_cast(u32x2, ob);
         }
       }
     if (p.lse && hh == 0)
-      p.lse[static_cast<size_t>(bh) * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+      p.lse[static_cast<size_t>(bh) * N + qi] = (st.m_run + log2f(l_tot)) * kLn2;
   }
 }
 

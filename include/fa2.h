@@ -65,10 +65,13 @@ extern "C" {
 #define FA2_ERR_HIP (-7)     /* the kernel launch failed (hipGetLastError)     */
 
 /* Size limits (FA2_ERR_SHAPE beyond them): B*H*N*d <= FA2_MAX_ELEMS elements
-   per tensor (2^40, far above one GPU's memory); N*d, B*H and the number of
-   workgroups (B*H*ceil(N/128), or ceil(N/64) for fa2_fwd_fp32) each
-   <= 2^31 - 1, because per-head offsets and grid indices are 32-bit. */
+   per tensor (2^40, far above one GPU's memory); B*H and the number of
+   workgroups (B*H*ceil(N/128), or B*H*ceil(N/64) for fa2_fwd_fp32) each
+   <= 2^31 - 1 (32-bit grid indices); N*d <= FA2_MAX_HEAD_ELEMS_BF16 for the
+   bf16 entry points (one head is addressed with 32-bit byte offsets) and
+   <= 2^31 - 1 for fa2_fwd_fp32. */
 #define FA2_MAX_ELEMS (1LL << 40)
+#define FA2_MAX_HEAD_ELEMS_BF16 ((1LL << 30) - (1LL << 16))
 
 /*
  * fa2_fwd -- bf16 inputs, bf16 output.
