@@ -38,19 +38,19 @@
 //    each lane holds ONE query (lane % 32) and 16 keys, so the row max and
 //    row sum are in-lane reductions plus a single v_permlane32_swap between
 //    the two half-waves, and the rescale factor is a per-lane scalar.
-//  * The K rows feeding MFMA row m are permuted (bits 2 and 3 of m swapped)
-//    so that the eight keys a lane holds for each 16-key step are contiguous;
-//    the fp32 result registers then convert directly into the B operand of
-//    O^T += V^T P^T, and V^T is read with one 16-byte LDS load per operand.
-//  * K is staged row-major and V transposed (V^T, keys contiguous) in LDS,
-//    both with XOR swizzles of their 16-byte chunks so that every 8-lane
-//    phase of a 128-bit LDS access touches 32 distinct banks.  Swizzles use
-//    only lane bits that leave compile-time parts of the address additive,
-//    so almost every LDS access is a per-lane base plus an immediate.
-//  * Global loads are raw buffer loads with the per-head extent as the
-//    buffer size: rows past the end of the sequence read as zero in hardware,
-//    with no branches.  The next tile is fetched into registers while the
-//    current one is consumed; LDS is double-buffered, one barrier per tile.
+//  * K and V go from HBM straight into LDS (buffer_load ... lds: no register
+//    staging), issued one tile ahead and double-buffered, one barrier per
+//    tile.  The loads are raw buffer loads with the per-head extent as the
+//    buffer size, so rows past the end of the sequence read as zero in
+//    hardware, with no branches.
+//  * K is stored row-major with its 16-byte granules XOR-swizzled by the row,
+//    so the 16 lanes of each phase of a 128-bit read hit 16 distinct bank
+//    groups.  V is stored in blocks of 32 columns (each key's 64 bytes
+//    contiguous inside a block) and read with ds_read_b64_tr_b16, which
+//    transposes 16-lane groups in flight: each lane receives one column of
+//    four consecutive keys, exactly the A operand of O^T += V^T P^T, whose B
+//    operand is the S^T result converted in place to bf16.  All V reads are
+//    one per-lane base plus immediates, and conflict-free.
 //  * Causal: tiles past a wave's last query are skipped by that wave (it only
 //    helps to stage them); the mask is applied only in the tiles that cross
 //    the diagonal or the ragged end of the sequence, which run in a separate
@@ -69,10 +69,13 @@ namespace fa2 {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 256;
 constexpr int kRows = kBf16RowsPerBlock;  // 128 query rows per workgroup
@@ -95,27 +98,22 @@ struct Params {
 template <int D>
 struct Cfg {
   static constexpr int BC = (D == 128) ? 64 : 128;  // keys per tile
-  static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
+  static constexpr int KCH = D / 8;                 // 16-byte granules per K row
   static constexpr int NKT = BC / 32;               // 32-key sub-tiles
   static constexpr int NDT = D / 16;                // 16-dim MFMA k-steps
   static constexpr int NCT = D / 32;                // 32-wide O^T row tiles
-  static constexpr int KLOADS = BC * KCH / kThreads;
-  static constexpr int VCOLS = D / 4;               // 4-column V groups
-  static constexpr int TILE = BC * D;               // elements per K or V tile
-  static constexpr int TILE_BYTES = TILE * 2;       // 16 KB either way
-  static_assert(KLOADS * kThreads == BC * KCH, "K tile split");
-  static_assert((BC / 8) * VCOLS == kThreads, "V tile split");
-  static_assert(kThreads / KCH * D * 2 == 4096, "K load stride");
+  static constexpr int TILE_BYTES = BC * D * 2;     // 16 KB for K or V
+  static constexpr int K_ROWS_PER_LOAD = 64 / KCH;  // rows per 1 KB wave load
+  static_assert(TILE_BYTES == 16 * 1024, "one tile = 16 wave loads of 1 KB");
 };
 
-// Row permutation inside each 16-row group: swap bits 2 and 3.
-__device__ __forceinline__ int perm16(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+// K granule swizzle: granule j of row r is stored at position j ^ kswz(r).
+// With 16 granules per row (d = 128) one row fills the 64 banks; with 8
+// (d = 64) two rows share them, so the row pair index is used.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
-
-// Swizzle of V^T rows (columns of V): 16-byte chunk j of row c is stored at
-// chunk j ^ vsw(c).  It uses bits 0-4 of c only, so rows 32 apart share it.
-__device__ __forceinline__ int vsw(int c) { return (c & 7) ^ ((c >> 3) & 3); }
 
 // (x of lanes 0-31, x of lanes 32-63) as seen from every lane.
 __device__ __forceinline__ void halves(float x, float &lo, float &hi) {
@@ -133,9 +131,12 @@ template <typename T>
 __device__ __forceinline__ T lds_load(const char *base, int byte_off) {
   return *reinterpret_cast<const T *>(base + byte_off);
 }
-template <typename T>
-__device__ __forceinline__ void lds_store(char *base, int byte_off, T v) {
-  *reinterpret_cast<T *>(base + byte_off) = v;
+
+// Transposing LDS read: within each group of 16 lanes, lane L receives
+// element L % 4 of the 8-byte chunks addressed by lanes 4e + L / 4, e = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr(const char *base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(base + byte_off));
 }
 
 // Everything one wave needs while it walks the K/V tiles.
@@ -147,80 +148,63 @@ struct WaveState {
   float l_run;  // this half-wave's share of the running sum
 };
 
-// Per-thread byte offsets that stay fixed for the whole kernel.
+// Per-thread byte offsets fixed for the whole kernel.
 template <int D>
 struct Offsets {
-  int k_rd[4];  // K operand reads, 16-dim steps 0..3 (steps 4..7 at +128 B)
-  int v_rd[4];  // V^T operand reads, (sub-tile parity, 16-key half) 0..3
-  int k_wr;     // K staging write (loads it = 0..3 at +4096 B each)
-  int v_wr[4];  // V^T staging writes, columns 4*vcc + e
-  int k_ld;     // K buffer-load offset within a tile
-  int v_ld;     // V buffer-load offset within a tile (rows r at +r*D*2)
+  int k_rd[Cfg<D>::NDT];  // K operand reads per 16-dim step
+  int v_rd;               // V transposed reads (all others are immediates)
+  int k_ld[4];            // K loads within a tile, one per wave load
+  int v_ld;               // V loads within a tile (wave load it at +it*VSTEP)
 };
 
+// The four 1 KB loads of K and the four of V this wave issues for one tile.
+// LDS destinations are wave-uniform (they go to M0).
 template <int D>
-__device__ __forceinline__ void gload(const __amdgpu_buffer_rsrc_t &rk,
-                                      const __amdgpu_buffer_rsrc_t &rv,
-                                      const Offsets<D> &off, int tile_byte,
-                                      u32x4 (&kpre)[Cfg<D>::KLOADS],
-                                      u32x2 (&vpre)[8]) {
-#pragma unroll
-  for (int it = 0; it < Cfg<D>::KLOADS; ++it)
-    kpre[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off.k_ld,
-                                                     tile_byte + it * 4096, 0);
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-    vpre[r] = __builtin_amdgcn_raw_buffer_load_b64(rv, off.v_ld + r * D * 2,
-                                                   tile_byte, 0);
-}
-
-template <int D, int BUF>
-__device__ __forceinline__ void swrite(char *smem, const Offsets<D> &off,
-                                       const u32x4 (&kpre)[Cfg<D>::KLOADS],
-                                       const u32x2 (&vpre)[8]) {
+__device__ __forceinline__ void issue_loads(__amdgpu_buffer_rsrc_t rk,
+                                            __amdgpu_buffer_rsrc_t rv,
+                                            const Offsets<D> &off, char *kbuf,
+                                            char *vbuf, int wv, int tile_byte) {
   using C = Cfg<D>;
-  char *kb = smem + BUF * C::TILE_BYTES;
-  char *vb = smem + (2 + BUF) * C::TILE_BYTES;
 #pragma unroll
-  for (int it = 0; it < C::KLOADS; ++it) lds_store(kb, off.k_wr + it * 4096, kpre[it]);
-  // 8 keys x 4 columns -> 4 columns x 8 keys (bf16 transpose in registers)
+  for (int it = 0; it < 4; ++it) {
+    const int inst = 4 * wv + it;
+    const int vo = off.k_ld[it];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rk, (lds_void *)(kbuf + inst * 1024), 16, vo, tile_byte, 0, 0);
+  }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    u32x4 outv;
-#pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      const uint32_t a = (e < 2) ? vpre[2 * pr].x : vpre[2 * pr].y;
-      const uint32_t b = (e < 2) ? vpre[2 * pr + 1].x : vpre[2 * pr + 1].y;
-      outv[pr] = (e & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                         : __builtin_amdgcn_perm(b, a, 0x05040100u);
-    }
-    lds_store(vb, off.v_wr[e], outv);
+  for (int it = 0; it < 4; ++it) {
+    // d = 128: block of 32 columns = wave, 16-key group = it;
+    // d = 64: block = wave / 2, 16-key group = 4 * (wave & 1) + it
+    const int cg = (D == 128) ? wv : (wv >> 1);
+    const int kb = (D == 128) ? it : (4 * (wv & 1) + it);
+    const int vo = off.v_ld;
+    const int so = tile_byte + it * 16 * D * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rv, (lds_void *)(vbuf + cg * C::BC * 64 + kb * 1024), 16, vo, so, 0, 0);
   }
 }
 
 // One K/V tile for one wave.  MASKED tiles apply the causal / sequence-end
 // mask; unmasked tiles need no compare at all.
-template <int D, bool CAUSAL, bool MASKED, int BUF>
-__device__ __forceinline__ void tile(const char *smem, const Offsets<D> &off,
-                                     WaveState<D> &st, float c, int j0, int N,
-                                     int qi, int hh) {
+template <int D, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void tile(const char *kb, const char *vb,
+                                     const Offsets<D> &off, WaveState<D> &st,
+                                     float c, int j0, int N, int qi, int hh) {
   using C = Cfg<D>;
-  const char *kb = smem + BUF * C::TILE_BYTES;
-  const char *vb = smem + (2 + BUF) * C::TILE_BYTES;
 
-  // -- S^T = K Q^T ---------------------------------------------------------
+  // -- S^T = K Q^T: MFMA row m of sub-tile kt is key j0 + 32kt + m ---------
   f32x16 s[C::NKT];
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-    // operands in groups of four: 16 registers in flight, not 32
 #pragma unroll
     for (int g = 0; g < C::NDT; g += 4) {
       bf16x8 a[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = lds_load<bf16x8>(kb, off.k_rd[i] + (g >> 2) * 128 + kt * 32 * D * 2);
+        a[i] = lds_load<bf16x8>(kb, off.k_rd[g + i] + kt * 32 * D * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], st.qreg[g + i],
@@ -228,18 +212,18 @@ __device__ __forceinline__ void tile(const char *smem, const Offsets<D> &off,
     }
   }
 
-  // -- mask: register r of sub-tile kt holds key j0 + 32kt + 16(r/8) + 8hh + r%8
+  // -- mask: register r of sub-tile kt holds key j0 + 32kt + 8(r/4) + 4hh + r%4
   if (MASKED) {
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j0 + 32 * kt + 16 * (r >> 3) + 8 * hh + (r & 7);
+        const int key = j0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (key >= N || (CAUSAL && key > qi)) s[kt][r] = -INFINITY;
       }
   }
 
-  // -- online softmax --------------------------------------------------------
+  // -- online softmax ------------------------------------------------------
   float mx = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt)
@@ -262,6 +246,9 @@ __device__ __forceinline__ void tile(const char *smem, const Offsets<D> &off,
   }
   const float mu = (MASKED && st.m_run == -INFINITY) ? 0.f : st.m_run;
 
+  // P~ in bf16; 16-key step u of sub-tile kt uses registers 8u..8u+7, i.e.
+  // keys 32kt + 16u + 8a + 4hh + b for element 4a + b: the B operand of the
+  // P.V MFMA (k index 8hh + 4a + b) with no data movement.
   bf16x8 pb[C::NKT][2];
   float rs = 0.f;
 #pragma unroll
@@ -278,16 +265,20 @@ __device__ __forceinline__ void tile(const char *smem, const Offsets<D> &off,
       }
   st.l_run += rs;
 
-  // -- O^T += V^T P^T ----------------------------------------------------------
+  // -- O^T += V^T P^T: A operand = columns 32ct + lane%32 of the keys above --
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       bf16x8 a[C::NCT];
 #pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct)
-        a[ct] = lds_load<bf16x8>(vb, off.v_rd[(kt & 1) * 2 + u] + (kt >> 1) * 128 +
-                                         ct * 32 * C::BC * 2);
+      for (int ct = 0; ct < C::NCT; ++ct) {
+        const int imm = ct * C::BC * 64 + (32 * kt + 16 * u) * 64;
+        const s16x4 lo = lds_read_tr(vb, off.v_rd + imm);
+        const s16x4 hi = lds_read_tr(vb, off.v_rd + imm + 8 * 64);
+        a[ct] = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
 #pragma unroll
       for (int ct = 0; ct < C::NCT; ++ct)
         st.oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ct], pb[kt][u],
@@ -298,11 +289,12 @@ __device__ __forceinline__ void tile(const char *smem, const Offsets<D> &off,
 template <int D, bool CAUSAL, bool O32>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[4 * C::TILE_BYTES];
+  // [K buffer 0][K buffer 1][V buffer 0][V buffer 1], 16 KB each
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31;  // query column of this lane in S^T / O^T
   const int hh = lane >> 5;  // half-wave
 
@@ -317,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
 
   const int N = p.n;
   const size_t head = static_cast<size_t>(bh) * N * D;
-  const int head_bytes = N * D * 2;  // < 2^32 - 2^17 (host-validated)
+  const int head_bytes = N * D * 2;  // < 2^31 (host-validated)
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(p.q + head), 0, head_bytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -332,22 +324,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // ---- fixed offsets -------------------------------------------------------
   Offsets<D> off;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    off.k_rd[i] = (perm16(lr) * D + (((2 * i + hh) ^ (lr & 7)) * 8)) * 2;
-    const int chunk = 2 * i + hh;  // (sub-tile parity, half) -> 16-B chunk
-    off.v_rd[i] = (lr * C::BC + ((chunk ^ vsw(lr)) * 8)) * 2;
+  for (int dt = 0; dt < C::NDT; ++dt)
+    off.k_rd[dt] = (lr * D + (((2 * dt + hh) ^ kswz<D>(lr)) * 8)) * 2;
+  {
+    // transposed V reads: lane s of a 16-lane group g supplies key 4hh + s/4
+    // (plus the step's base key) and columns 16(g&1) + 4(s%4) .. +3
+    const int g = lane >> 4, sl = lane & 15;
+    off.v_rd = (4 * hh + (sl >> 2)) * 64 + (g & 1) * 32 + (sl & 3) * 8;
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int row = (4 * wv + it) * C::K_ROWS_PER_LOAD + lane / C::KCH;
+    const int pos = lane % C::KCH;
+    off.k_ld[it] = row * D * 2 + ((pos ^ kswz<D>(row)) * 16);
   }
   {
-    const int row = tid / C::KCH, ch = tid % C::KCH;
-    off.k_wr = (row * D + ((ch ^ (perm16(row) & 7)) * 8)) * 2;
-    off.k_ld = (row * D + ch * 8) * 2;
-    const int vcc = tid % C::VCOLS, vjg = tid / C::VCOLS;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int col = vcc * 4 + e;
-      off.v_wr[e] = (col * C::BC + ((vjg ^ vsw(col)) * 8)) * 2;
-    }
-    off.v_ld = ((vjg * 8) * D + vcc * 4) * 2;
+    const int cg = (D == 128) ? wv : (wv >> 1);
+    const int kb0 = (D == 128) ? 0 : 4 * (wv & 1);
+    off.v_ld = (16 * kb0 + lane / 4) * D * 2 + (4 * cg + (lane & 3)) * 16;
   }
 
   // ---- Q into registers (B operand of S^T = K Q^T) -------------------------
@@ -379,23 +373,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int ntiles = (kend + C::BC - 1) / C::BC;
   int n_full = CAUSAL ? (q0 + 1) / C::BC : N / C::BC;
   if (n_full > ntiles) n_full = ntiles;
-  if (n_full * C::BC > N) n_full = N / C::BC;
 
-  u32x4 kpre[C::KLOADS];
-  u32x2 vpre[8];
-  gload<D>(rk, rv, off, 0, kpre, vpre);
-  swrite<D, 0>(smem, off, kpre, vpre);
+  char *kbuf0 = smem, *kbuf1 = smem + C::TILE_BYTES;
+  char *vbuf0 = smem + 2 * C::TILE_BYTES, *vbuf1 = smem + 3 * C::TILE_BYTES;
+
+  // Rows past the end of the sequence load as zeros; clear LDS first so that
+  // no tile can ever expose uninitialised bits, whatever the hardware does
+  // with out-of-range lanes.
+  if (N % C::BC != 0) {
+    for (int i = tid; i < 4 * C::TILE_BYTES / 16; i += kThreads)
+      reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+  issue_loads<D>(rk, rv, off, kbuf0, vbuf0, wv, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   auto step = [&](auto buf_tag, auto masked_tag, int t) {
     constexpr int BUF = decltype(buf_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int j0 = t * C::BC;
-    const bool more = t + 1 < ntiles;
-    if (more) gload<D>(rk, rv, off, (j0 + C::BC) * D * 2, kpre, vpre);
+    if (t + 1 < ntiles)
+      issue_loads<D>(rk, rv, off, BUF ? kbuf0 : kbuf1, BUF ? vbuf0 : vbuf1, wv,
+                     (j0 + C::BC) * D * 2);
     if (!MASKED || !CAUSAL || j0 <= qw + 31)
-      tile<D, CAUSAL, MASKED, BUF>(smem, off, st, c, j0, N, qi, hh);
-    if (more) swrite<D, 1 - BUF>(smem, off, kpre, vpre);
+      tile<D, CAUSAL, MASKED>(BUF ? kbuf1 : kbuf0, BUF ? vbuf1 : vbuf0, off, st,
+                              c, j0, N, qi, hh);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   using B0 = std::integral_constant<int, 0>;
