@@ -157,14 +157,12 @@ struct Offsets {
   int v_ld;               // V loads within a tile (wave load it at +it*VSTEP)
 };
 
-// The four 1 KB loads of K and the four of V this wave issues for one tile.
+// The four 1 KB loads of K, and of V, that this wave issues for one tile.
 // LDS destinations are wave-uniform (they go to M0).
 template <int D>
-__device__ __forceinline__ void issue_loads(__amdgpu_buffer_rsrc_t rk,
-                                            __amdgpu_buffer_rsrc_t rv,
-                                            const Offsets<D> &off, char *kbuf,
-                                            char *vbuf, int wv, int tile_byte) {
-  using C = Cfg<D>;
+__device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t rk,
+                                        const Offsets<D> &off, char *kbuf,
+                                        int wv, int tile_byte) {
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int inst = 4 * wv + it;
@@ -172,6 +170,13 @@ __device__ __forceinline__ void issue_loads(__amdgpu_buffer_rsrc_t rk,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rk, (lds_void *)(kbuf + inst * 1024), 16, vo, tile_byte, 0, 0);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv,
+                                        const Offsets<D> &off, char *vbuf,
+                                        int wv, int tile_byte) {
+  using C = Cfg<D>;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     // d = 128: block of 32 columns = wave, 16-key group = it;
@@ -185,16 +190,12 @@ __device__ __forceinline__ void issue_loads(__amdgpu_buffer_rsrc_t rk,
   }
 }
 
-// One K/V tile for one wave.  MASKED tiles apply the causal / sequence-end
-// mask; unmasked tiles need no compare at all.
-template <int D, bool CAUSAL, bool MASKED>
-__device__ __forceinline__ void tile(const char *kb, const char *vb,
-                                     const Offsets<D> &off, WaveState<D> &st,
-                                     float c, int j0, int N, int qi, int hh) {
+// S^T = K Q^T for one tile: MFMA row m of sub-tile kt is key j0 + 32kt + m.
+template <int D>
+__device__ __forceinline__ void scores(const char *kb, const Offsets<D> &off,
+                                       const bf16x8 (&qreg)[Cfg<D>::NDT],
+                                       f32x16 (&s)[Cfg<D>::NKT]) {
   using C = Cfg<D>;
-
-  // -- S^T = K Q^T: MFMA row m of sub-tile kt is key j0 + 32kt + m ---------
-  f32x16 s[C::NKT];
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt) {
 #pragma unroll
@@ -207,12 +208,20 @@ __device__ __forceinline__ void tile(const char *kb, const char *vb,
         a[i] = lds_load<bf16x8>(kb, off.k_rd[g + i] + kt * 32 * D * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], st.qreg[g + i],
-                                                        s[kt], 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qreg[g + i], s[kt],
+                                                        0, 0, 0);
     }
   }
+}
 
-  // -- mask: register r of sub-tile kt holds key j0 + 32kt + 8(r/4) + 4hh + r%4
+// Mask (MASKED tiles only), row max, and the lazy rescale of (l, O~).
+// Returns the reference max to subtract in the exponent.
+template <int D, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ float softmax_max(f32x16 (&s)[Cfg<D>::NKT],
+                                             WaveState<D> &st, float c, int j0,
+                                             int N, int qi, int hh) {
+  using C = Cfg<D>;
+  // register r of sub-tile kt holds key j0 + 32kt + 8(r/4) + 4hh + r%4
   if (MASKED) {
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
@@ -222,8 +231,6 @@ __device__ __forceinline__ void tile(const char *kb, const char *vb,
         if (key >= N || (CAUSAL && key > qi)) s[kt][r] = -INFINITY;
       }
   }
-
-  // -- online softmax ------------------------------------------------------
   float mx = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt)
@@ -244,12 +251,20 @@ __device__ __forceinline__ void tile(const char *kb, const char *vb,
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.oacc[ct][r] *= alpha;
   }
-  const float mu = (MASKED && st.m_run == -INFINITY) ? 0.f : st.m_run;
+  return (MASKED && st.m_run == -INFINITY) ? 0.f : st.m_run;
+}
 
-  // P~ in bf16; 16-key step u of sub-tile kt uses registers 8u..8u+7, i.e.
-  // keys 32kt + 16u + 8a + 4hh + b for element 4a + b: the B operand of the
-  // P.V MFMA (k index 8hh + 4a + b) with no data movement.
-  bf16x8 pb[C::NKT][2];
+// P~ = 2^(S c - mu), summed in fp32 into l (the log-sum-exp needs the
+// unrounded values) and rounded to bf16 for the P.V product.  16-key step u
+// of sub-tile kt takes registers 8u..8u+7: keys 32kt + 16u + 8a + 4hh + b for
+// element 4a + b, which is the B operand of the P.V MFMA (k index
+// 8hh + 4a + b) as it is.
+template <int D, bool MASKED>
+__device__ __forceinline__ void softmax_exp(const f32x16 (&s)[Cfg<D>::NKT],
+                                            float mu, float c,
+                                            bf16x8 (&pb)[Cfg<D>::NKT][2],
+                                            float &l_run) {
+  using C = Cfg<D>;
   float rs = 0.f;
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt)
@@ -263,9 +278,16 @@ __device__ __forceinline__ void tile(const char *kb, const char *vb,
         rs += x;
         pb[kt][u][e] = static_cast<__bf16>(x);
       }
-  st.l_run += rs;
+  l_run += rs;
+}
 
-  // -- O^T += V^T P^T: A operand = columns 32ct + lane%32 of the keys above --
+// O^T += V^T P^T: A operand = columns 32ct + lane%32 of the keys above,
+// read transposed from LDS.
+template <int D>
+__device__ __forceinline__ void pv(const char *vb, const Offsets<D> &off,
+                                   const bf16x8 (&pb)[Cfg<D>::NKT][2],
+                                   f32x16 (&oacc)[Cfg<D>::NCT]) {
+  using C = Cfg<D>;
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
@@ -281,8 +303,8 @@ __device__ __forceinline__ void tile(const char *kb, const char *vb,
       }
 #pragma unroll
       for (int ct = 0; ct < C::NCT; ++ct)
-        st.oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ct], pb[kt][u],
-                                                              st.oacc[ct], 0, 0, 0);
+        oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ct], pb[kt][u],
+                                                           oacc[ct], 0, 0, 0);
     }
 }
 
@@ -367,15 +389,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   st.l_run = 0.f;
 
   // ---- tile schedule -------------------------------------------------------
+  // Software pipeline: iteration t computes the scores of tile t+1 (K one tile
+  // ahead in LDS) while it runs the softmax of tile t and the P.V product
+  // with V(t); the loads of K(t+2) and V(t+1) are in flight meanwhile.
   // Tiles [0, n_full) need no mask for any row of the block; the rest (the
   // diagonal band when causal, the ragged end of the sequence) are masked.
   const int kend = CAUSAL ? min(N, q0 + kRows) : N;
   const int ntiles = (kend + C::BC - 1) / C::BC;
   int n_full = CAUSAL ? (q0 + 1) / C::BC : N / C::BC;
   if (n_full > ntiles) n_full = ntiles;
+  // tiles this wave needs (causal: keys up to its last query)
+  const int w_tiles = CAUSAL ? min(ntiles, (qw + 31) / C::BC + 1) : ntiles;
+  // branch-free main loop: unmasked tile t with tile t+1 existing
+  const int n_main = min(n_full, ntiles - 1);
 
-  char *kbuf0 = smem, *kbuf1 = smem + C::TILE_BYTES;
-  char *vbuf0 = smem + 2 * C::TILE_BYTES, *vbuf1 = smem + 3 * C::TILE_BYTES;
+  auto kbuf = [&](int i) { return smem + i * C::TILE_BYTES; };
+  auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE_BYTES; };
 
   // Rows past the end of the sequence load as zeros; clear LDS first so that
   // no tile can ever expose uninitialised bits, whatever the hardware does
@@ -385,42 +414,64 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
   }
-  issue_loads<D>(rk, rv, off, kbuf0, vbuf0, wv, 0);
+  // prologue: K(0), V(0) -> buffers 0; then K(1) in flight while S(0) is
+  // computed.
+  issue_k<D>(rk, off, kbuf(0), wv, 0);
+  issue_v<D>(rv, off, vbuf(0), wv, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (ntiles > 1) issue_k<D>(rk, off, kbuf(1), wv, C::BC * D * 2);
+  f32x16 sa[C::NKT], sb[C::NKT];
+  scores<D>(kbuf(0), off, st.qreg, sa);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  auto step = [&](auto buf_tag, auto masked_tag, int t) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // one pipelined iteration; CUR holds S(t), NXT receives S(t+1)
+  auto step = [&](auto par_tag, int t, f32x16(&cur)[C::NKT],
+                  f32x16(&nxt)[C::NKT]) {
+    constexpr int P = decltype(par_tag)::value;  // t & 1
     const int j0 = t * C::BC;
-    if (t + 1 < ntiles)
-      issue_loads<D>(rk, rv, off, BUF ? kbuf0 : kbuf1, BUF ? vbuf0 : vbuf1, wv,
-                     (j0 + C::BC) * D * 2);
-    if (!MASKED || !CAUSAL || j0 <= qw + 31)
-      tile<D, CAUSAL, MASKED>(BUF ? kbuf1 : kbuf0, BUF ? vbuf1 : vbuf0, off, st,
-                              c, j0, N, qi, hh);
+    if (t + 2 < ntiles) issue_k<D>(rk, off, kbuf(P), wv, (j0 + 2 * C::BC) * D * 2);
+    issue_v<D>(rv, off, vbuf(1 - P), wv, (j0 + C::BC) * D * 2);
+    scores<D>(kbuf(1 - P), off, st.qreg, nxt);
+    const float mu = softmax_max<D, CAUSAL, false>(cur, st, c, j0, N, qi, hh);
+    bf16x8 pb[C::NKT][2];
+    softmax_exp<D, false>(cur, mu, c, pb, st.l_run);
+    pv<D>(vbuf(P), off, pb, st.oacc);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  using Unmasked = std::integral_constant<bool, false>;
-  using Masked = std::integral_constant<bool, true>;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
 
   int t = 0;
-  for (; t + 2 <= n_full; t += 2) {
-    step(B0{}, Unmasked{}, t);
-    step(B1{}, Unmasked{}, t + 1);
+  for (; t + 2 <= n_main; t += 2) {
+    step(P0{}, t, sa, sb);
+    step(P1{}, t + 1, sb, sa);
   }
-  if (t < n_full) {
-    step(B0{}, Unmasked{}, t);
+  if (t < n_main) {
+    step(P0{}, t, sa, sb);
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt) sa[kt] = sb[kt];
     ++t;
   }
+  // general loop: masked tiles, waves that stop early, the last tile
   for (; t < ntiles; ++t) {
-    if (t & 1)
-      step(B1{}, Masked{}, t);
-    else
-      step(B0{}, Masked{}, t);
+    const int j0 = t * C::BC;
+    const int p = t & 1;
+    if (t + 2 < ntiles) issue_k<D>(rk, off, kbuf(p), wv, (j0 + 2 * C::BC) * D * 2);
+    if (t + 1 < ntiles) issue_v<D>(rv, off, vbuf(1 - p), wv, (j0 + C::BC) * D * 2);
+    if (t + 1 < w_tiles) scores<D>(kbuf(1 - p), off, st.qreg, sb);
+    if (t < w_tiles) {
+      const float mu = softmax_max<D, CAUSAL, true>(sa, st, c, j0, N, qi, hh);
+      bf16x8 pb[C::NKT][2];
+      softmax_exp<D, true>(sa, mu, c, pb, st.l_run);
+      pv<D>(vbuf(p), off, pb, st.oacc);
+    }
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt) sa[kt] = sb[kt];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // ---- epilogue: O = O~ / l, lse ---------------------------------------------
