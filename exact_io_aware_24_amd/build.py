@@ -36,6 +36,8 @@ def hipcc() -> str:
 def compile_flags(extra=()) -> list:
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             "-fvisibility=hidden", "-Wall", "-Wno-unused-result",
+            # dma16() names M0 (reserved) as clobbered on purpose
+            "-Wno-inline-asm",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I" + INCLUDE, "-I" + CSRC] + list(extra)
 

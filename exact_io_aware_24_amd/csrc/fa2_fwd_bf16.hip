@@ -74,7 +74,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 256;
@@ -139,6 +138,40 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char *base, int byte_off) {
       (lds_s16x4 *)(base + byte_off));
 }
 
+// 16 bytes per lane from a raw buffer straight into LDS at lds_addr + 16 *
+// lane (buffer_load_dwordx4 ... lds; M0 holds the wave-uniform LDS address).
+// Issued through asm so that the compiler does not track it: it would
+// otherwise wait for every such load before the next LDS read of ANY buffer,
+// serialising the prefetch.  The kernel itself waits (vmcnt(0)) before the
+// barrier that publishes a filled buffer, which is the only ordering needed.
+__device__ __forceinline__ void dma16(u32x4 rsrc, int voff, int soff,
+                                      uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+// Raw buffer descriptor (words 0-3) for `bytes` bytes at `base`, made
+// wave-uniform so that it lives in scalar registers.
+__device__ __forceinline__ u32x4 make_desc(const void *base, int bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bytes));
+  r[3] = static_cast<uint32_t>(kBufWord3);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const char *)(p)));
+}
+
 // Everything one wave needs while it walks the K/V tiles.
 template <int D>
 struct WaveState {
@@ -160,20 +193,19 @@ struct Offsets {
 // The four 1 KB loads of K, and of V, that this wave issues for one tile.
 // LDS destinations are wave-uniform (they go to M0).
 template <int D>
-__device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t rk,
+__device__ __forceinline__ void issue_k(u32x4 rk,
                                         const Offsets<D> &off, char *kbuf,
                                         int wv, int tile_byte) {
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int inst = 4 * wv + it;
     const int vo = off.k_ld[it];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rk, (lds_void *)(kbuf + inst * 1024), 16, vo, tile_byte, 0, 0);
+    dma16(rk, vo, tile_byte, lds_addr(kbuf + inst * 1024));
   }
 }
 
 template <int D>
-__device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv,
+__device__ __forceinline__ void issue_v(u32x4 rv,
                                         const Offsets<D> &off, char *vbuf,
                                         int wv, int tile_byte) {
   using C = Cfg<D>;
@@ -185,8 +217,7 @@ __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv,
     const int kb = (D == 128) ? it : (4 * (wv & 1) + it);
     const int vo = off.v_ld;
     const int so = tile_byte + it * 16 * D * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rv, (lds_void *)(vbuf + cg * C::BC * 64 + kb * 1024), 16, vo, so, 0, 0);
+    dma16(rv, vo, so, lds_addr(vbuf + cg * C::BC * 64 + kb * 1024));
   }
 }
 
@@ -214,12 +245,19 @@ __device__ __forceinline__ void scores(const char *kb, const Offsets<D> &off,
   }
 }
 
-// Mask (MASKED tiles only), row max, and the lazy rescale of (l, O~).
-// Returns the reference max to subtract in the exponent.
+// Mask (MASKED tiles only), row max, and the lazy update of the reference
+// max for one tile of scores.  When a row's tile max exceeds the reference
+// by more than the threshold the whole wave raises it, rescales l and O~ by
+// the same factor (the merge is exact for any common reference) and goes
+// on; otherwise nothing changes and the exponentials of this tile are taken
+// against the old reference (they stay <= 2^8).  Called as soon as a tile's
+// scores exist, one iteration before their exponentials, so that the
+// iteration body that follows has no branch between its MFMAs and its
+// exponentials.
 template <int D, bool CAUSAL, bool MASKED>
-__device__ __forceinline__ float softmax_max(f32x16 (&s)[Cfg<D>::NKT],
-                                             WaveState<D> &st, float c, int j0,
-                                             int N, int qi, int hh) {
+__device__ __forceinline__ void softmax_max(f32x16 (&s)[Cfg<D>::NKT],
+                                            WaveState<D> &st, float c, int j0,
+                                            int N, int qi, int hh) {
   using C = Cfg<D>;
   // register r of sub-tile kt holds key j0 + 32kt + 8(r/4) + 4hh + r%4
   if (MASKED) {
@@ -251,7 +289,6 @@ __device__ __forceinline__ float softmax_max(f32x16 (&s)[Cfg<D>::NKT],
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.oacc[ct][r] *= alpha;
   }
-  return (MASKED && st.m_run == -INFINITY) ? 0.f : st.m_run;
 }
 
 // P~ = 2^(S c - mu), summed in fp32 into l (the log-sum-exp needs the
@@ -334,10 +371,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int head_bytes = N * D * 2;  // < 2^31 (host-validated)
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(p.q + head), 0, head_bytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(p.k + head), 0, head_bytes, kBufWord3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(p.v + head), 0, head_bytes, kBufWord3);
+  const u32x4 rk = make_desc(p.k + head, head_bytes);
+  const u32x4 rv = make_desc(p.v + head, head_bytes);
 
   const int q0 = qb * kRows;      // first query of the block
   const int qw = q0 + wv * 32;    // first query of this wave
@@ -400,8 +435,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   if (n_full > ntiles) n_full = ntiles;
   // tiles this wave needs (causal: keys up to its last query)
   const int w_tiles = CAUSAL ? min(ntiles, (qw + 31) / C::BC + 1) : ntiles;
-  // branch-free main loop: unmasked tile t with tile t+1 existing
-  const int n_main = min(n_full, ntiles - 1);
+  // branch-free main loop: tiles t and t+1 unmasked
+  const int n_main = min(n_full - 1, ntiles - 1);
 
   auto kbuf = [&](int i) { return smem + i * C::TILE_BYTES; };
   auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE_BYTES; };
@@ -423,6 +458,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   if (ntiles > 1) issue_k<D>(rk, off, kbuf(1), wv, C::BC * D * 2);
   f32x16 sa[C::NKT], sb[C::NKT];
   scores<D>(kbuf(0), off, st.qreg, sa);
+  if (n_full > 0)
+    softmax_max<D, CAUSAL, false>(sa, st, c, 0, N, qi, hh);
+  else
+    softmax_max<D, CAUSAL, true>(sa, st, c, 0, N, qi, hh);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -434,10 +473,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     if (t + 2 < ntiles) issue_k<D>(rk, off, kbuf(P), wv, (j0 + 2 * C::BC) * D * 2);
     issue_v<D>(rv, off, vbuf(1 - P), wv, (j0 + C::BC) * D * 2);
     scores<D>(kbuf(1 - P), off, st.qreg, nxt);
-    const float mu = softmax_max<D, CAUSAL, false>(cur, st, c, j0, N, qi, hh);
     bf16x8 pb[C::NKT][2];
-    softmax_exp<D, false>(cur, mu, c, pb, st.l_run);
+    softmax_exp<D, false>(cur, st.m_run, c, pb, st.l_run);
     pv<D>(vbuf(P), off, pb, st.oacc);
+    softmax_max<D, CAUSAL, false>(nxt, st, c, j0 + C::BC, N, qi, hh);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -463,11 +502,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     if (t + 1 < ntiles) issue_v<D>(rv, off, vbuf(1 - p), wv, (j0 + C::BC) * D * 2);
     if (t + 1 < w_tiles) scores<D>(kbuf(1 - p), off, st.qreg, sb);
     if (t < w_tiles) {
-      const float mu = softmax_max<D, CAUSAL, true>(sa, st, c, j0, N, qi, hh);
+      const float mu = (st.m_run == -INFINITY) ? 0.f : st.m_run;
       bf16x8 pb[C::NKT][2];
       softmax_exp<D, true>(sa, mu, c, pb, st.l_run);
       pv<D>(vbuf(p), off, pb, st.oacc);
     }
+    if (t + 1 < w_tiles)
+      softmax_max<D, CAUSAL, true>(sb, st, c, j0 + C::BC, N, qi, hh);
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt) sa[kt] = sb[kt];
     __builtin_amdgcn_s_waitcnt(0);
