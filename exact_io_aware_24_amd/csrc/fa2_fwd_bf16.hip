@@ -122,6 +122,15 @@ __device__ __forceinline__ void halves(float x, float &lo, float &hi) {
   hi = __uint_as_float(r[1]);
 }
 
+// Scheduling fence for LDS reads and MFMAs only: VALU, SALU, transcendental
+// and VMEM instructions may still be moved across it.  It pins operand
+// reads a whole MFMA group ahead of their consumers (the scheduler would
+// otherwise sink them to just before use, exposing LDS latency).
+__device__ __forceinline__ void pin_lds_mfma() {
+  __builtin_amdgcn_sched_barrier(0x0002 | 0x0004 | 0x0010 | 0x0020 | 0x0040 |
+                                 0x0200 | 0x0400);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
@@ -222,26 +231,37 @@ __device__ __forceinline__ void issue_v(u32x4 rv,
 }
 
 // S^T = K Q^T for one tile: MFMA row m of sub-tile kt is key j0 + 32kt + m.
+// The K operands are read from LDS one group of four ahead of the MFMAs
+// that consume them, so the LDS latency hides under the previous group.
 template <int D>
 __device__ __forceinline__ void scores(const char *kb, const Offsets<D> &off,
                                        const bf16x8 (&qreg)[Cfg<D>::NDT],
                                        f32x16 (&s)[Cfg<D>::NKT]) {
   using C = Cfg<D>;
+  constexpr int G = C::NDT / 4;   // groups of four k-steps per sub-tile
+  constexpr int NG = C::NKT * G;  // groups per tile
+  bf16x8 a[2][4];
 #pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt) {
+  for (int i = 0; i < 4; ++i) a[0][i] = lds_load<bf16x8>(kb, off.k_rd[i]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-    for (int g = 0; g < C::NDT; g += 4) {
-      bf16x8 a[4];
+  for (int grp = 0; grp < NG; ++grp) {
+    if (grp + 1 < NG) {
+      const int kt1 = (grp + 1) / G, g1 = ((grp + 1) % G) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = lds_load<bf16x8>(kb, off.k_rd[g + i] + kt * 32 * D * 2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qreg[g + i], s[kt],
-                                                        0, 0, 0);
+        a[(grp + 1) & 1][i] =
+            lds_load<bf16x8>(kb, off.k_rd[g1 + i] + kt1 * 32 * D * 2);
     }
+    pin_lds_mfma();
+    const int kt = grp / G, g = (grp % G) * 4;
+    if (g == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[grp & 1][i], qreg[g + i],
+                                                      s[kt], 0, 0, 0);
   }
 }
 
@@ -319,30 +339,34 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[Cfg<D>::NKT],
 }
 
 // O^T += V^T P^T: A operand = columns 32ct + lane%32 of the keys above,
-// read transposed from LDS.
+// read transposed from LDS one 16-key step ahead of the MFMAs that use it.
 template <int D>
 __device__ __forceinline__ void pv(const char *vb, const Offsets<D> &off,
                                    const bf16x8 (&pb)[Cfg<D>::NKT][2],
                                    f32x16 (&oacc)[Cfg<D>::NCT]) {
   using C = Cfg<D>;
+  constexpr int NS = 2 * C::NKT;  // 16-key steps per tile
+  bf16x8 a[2][C::NCT];
+  auto read = [&](int step, bf16x8 (&dst)[C::NCT]) {
 #pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bf16x8 a[C::NCT];
-#pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct) {
-        const int imm = ct * C::BC * 64 + (32 * kt + 16 * u) * 64;
-        const s16x4 lo = lds_read_tr(vb, off.v_rd + imm);
-        const s16x4 hi = lds_read_tr(vb, off.v_rd + imm + 8 * 64);
-        a[ct] = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct)
-        oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ct], pb[kt][u],
-                                                           oacc[ct], 0, 0, 0);
+    for (int ct = 0; ct < C::NCT; ++ct) {
+      const int imm = ct * C::BC * 64 + 16 * step * 64;
+      const s16x4 lo = lds_read_tr(vb, off.v_rd + imm);
+      const s16x4 hi = lds_read_tr(vb, off.v_rd + imm + 8 * 64);
+      dst[ct] = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
+  };
+  read(0, a[0]);
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    if (st + 1 < NS) read(st + 1, a[(st + 1) & 1]);
+    pin_lds_mfma();
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+      oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          a[st & 1][ct], pb[st >> 1][st & 1], oacc[ct], 0, 0, 0);
+  }
 }
 
 template <int D, bool CAUSAL, bool O32>
