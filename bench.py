@@ -116,8 +116,9 @@ def cpu_baseline(w, q, k, v, budget_s: float):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps; the engine clock needs ~0.5 s of load to settle")
     ap.add_argument("--workload", default=None,
                     help="workload name (default: the headline workload)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
