@@ -4,7 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 One step is one call of ``fa2_fwd`` (bf16 in, bf16 out, with lse) on the
-headline workload B=2, H=16, N=8192, d=128, causal, inputs resident in HBM.
+headline workload B=2, H=16, N=8192, d=128, causal, inputs resident in HBM
+(``--entry fa2_fwd_o32`` times the fp32-output sibling, ``--workload`` and
+``--seq-len`` pick another shape).
 W untimed warm-up steps are followed by exactly K timed steps between HIP
 events on the stream the kernel is launched on.  Rank 0 prints one JSON line:
 TFLOP/s (4*B*H*N^2*d, halved for causal), the roofline of the kernel against
@@ -12,11 +14,17 @@ the bf16 dense MFMA peak, the HBM traffic measured by rocprofv3 counters
 (when the committed counter summary matches the current kernel source), and
 the fp64 CPU oracle timed on a bounded sample of the same workload.
 
+``--per-call`` adds the median and minimum of single calls, each between its
+own pair of HIP events; ``--cold-mall MiB`` writes that much scratch memory
+between those calls so that the inputs are not left in the 256 MB
+last-level cache.
+
 Only one GPU is used: ``--gpus`` above 1 exits with a message.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -124,6 +132,14 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--entry", default="fa2_fwd", choices=("fa2_fwd", "fa2_fwd_o32"),
+                    help="entry point to time (o32: fp32 output)")
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="override the workload's sequence length")
+    ap.add_argument("--per-call", action="store_true",
+                    help="also time single calls (median, min)")
+    ap.add_argument("--cold-mall", type=int, default=0, metavar="MIB",
+                    help="with --per-call: write this many MiB between calls")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter "
                          "calibration runs)")
@@ -149,14 +165,21 @@ def main(argv=None):
     if w.dtype != "bf16":
         print("the benchmark times the bf16 path", file=sys.stderr)
         return 2
+    if args.seq_len:
+        if args.seq_len < 1:
+            print("--seq-len must be >= 1", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, N=args.seq_len)
     dev = torch.device("cuda:0")
-    q, k, v = wl.workload_inputs(w)
+    q, k, v = wl.make_inputs(w.B, w.H, w.N, w.d, w.dtype, outliers=w.outliers)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    o = torch.empty_like(qd)
+    out_dtype = torch.float32 if args.entry == "fa2_fwd_o32" else torch.bfloat16
+    o = torch.empty(qd.shape, dtype=out_dtype, device=dev)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
 
     def step():
-        fa2.forward(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        fa2.forward(qd, kd, vd, causal=w.causal, scale=w.scale,
+                    out_dtype=out_dtype, out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -177,7 +200,29 @@ def main(argv=None):
     ms = start.elapsed_time(end) / args.steps
     tflops = w.flops / (ms * 1e-3) / 1e12
 
-    traffic = read_traffic(name)
+    per_call = None
+    if args.per_call:
+        scratch = (torch.empty(args.cold_mall * (1 << 20) // 4, dtype=torch.float32,
+                               device=dev) if args.cold_mall else None)
+        pairs = []
+        for i in range(args.steps):
+            if scratch is not None:
+                scratch.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) for a, b in pairs)
+        per_call = {"median_ms": round(per[len(per) // 2], 5),
+                    "min_ms": round(per[0], 5),
+                    "median_tflops": round(w.flops / (per[len(per) // 2] * 1e-3) / 1e12, 3),
+                    "cold_mall_mib": args.cold_mall}
+
+    same_shape = not args.seq_len and args.entry == "fa2_fwd"
+    traffic = read_traffic(name) if same_shape else None
     rec = {
         "metric": "attention fwd TFLOP/s (1 MI355X) and % of bf16 MFMA peak",
         "value": round(tflops, 3),
@@ -193,7 +238,7 @@ def main(argv=None):
         "data": "synthetic (seeded randn, bf16)",
         "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale,
-                   "flops_per_step": w.flops, "entry_point": "fa2_fwd"},
+                   "flops_per_step": w.flops, "entry_point": args.entry},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 3),
@@ -208,6 +253,8 @@ def main(argv=None):
         "kernel_source_sha256": kernel_source_hash(),
         "gpu": torch.cuda.get_device_name(dev),
     }
+    if per_call is not None:
+        rec["per_call"] = per_call
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
     print(json.dumps(rec), flush=True)
