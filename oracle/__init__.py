@@ -11,7 +11,10 @@ each step follows, is stated in the C file's header:
 
 * ``S = scale * Q K^T`` row by row, causal keys ``j > i`` at ``-inf``;
 * ``P = softmax(S)`` with the row maximum subtracted first;
-* ``O = P V`` and ``lse = m + ln(sum exp(S - m))`` (natural log).
+* ``O = P V`` and ``lse = m + ln(sum exp(S - m))`` (natural log);
+* the exact gradients ``dQ, dK, dV`` of that definition for an incoming
+  gradient ``dO`` (``dV = P^T dO``, ``dS = P * (dO V^T - D)``,
+  ``dQ = scale dS K``, ``dK = scale dS^T Q``, ``D_i = sum_j P_ij dP_ij``).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms,
 invariants, the two-block merge rule from the online-softmax section of the
@@ -84,6 +87,11 @@ class OracleLib:
         lib.oracle_probs_f64.argtypes = [dp, dp, i64, i64, i64, ctypes.c_double,
                                          ctypes.c_int, dp, dp, dp]
         lib.oracle_probs_f64.restype = ctypes.c_int
+        lib.oracle_attention_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp,
+                                                 dp, i64, i64, i64, i64,
+                                                 ctypes.c_double, ctypes.c_int,
+                                                 ctypes.c_int]
+        lib.oracle_attention_bwd_f64.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         lib.oracle_default_threads.restype = ctypes.c_int
         self.path = path
@@ -143,6 +151,36 @@ class OracleLib:
             raise RuntimeError("oracle_attention_rows_f64 failed (%d)" % rc)
         return o, lse, rc
 
+    def attention_bwd(self, q, k, v, dout, scale: float, causal: bool = False,
+                      nthreads: int = 0):
+        """Exact gradients of every head for the incoming gradient ``dout``
+        of the output.
+
+        ``q``, ``dout``: ``[..., Nq, d]``; ``k``, ``v``: ``[..., Nk, d]``.
+        Returns ``(dq, dk, dv, delta, threads_used)`` (float64) where
+        ``delta[..., i] = sum_j P_ij dP_ij``.
+        """
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        if q.ndim < 2 or k.shape != v.shape or q.shape != dout.shape or \
+                q.shape[:-2] != k.shape[:-2] or q.shape[-1] != k.shape[-1]:
+            raise ValueError("shape mismatch: q %s k %s v %s dout %s"
+                             % (q.shape, k.shape, v.shape, dout.shape))
+        lead = q.shape[:-2]
+        nq, d = q.shape[-2], q.shape[-1]
+        nk = k.shape[-2]
+        nh = int(np.prod(lead)) if lead else 1
+        dq = np.empty(q.shape, dtype=np.float64)
+        dk = np.empty(k.shape, dtype=np.float64)
+        dv = np.empty(v.shape, dtype=np.float64)
+        delta = np.empty(lead + (nq,), dtype=np.float64)
+        rc = self._lib.oracle_attention_bwd_f64(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(delta), nh, nq, nk, d, float(scale), int(bool(causal)),
+            int(nthreads))
+        if rc < 0:
+            raise RuntimeError("oracle_attention_bwd_f64 failed (%d)" % rc)
+        return dq, dk, dv, delta, rc
+
     def probs(self, q, k, scale: float, causal: bool = False):
         """The probability matrix of ONE head: ``(P [Nq, Nk], m [Nq], l [Nq])``
         where ``m`` is each row's maximum score and ``l = sum_j exp(s_j - m)``.
@@ -189,3 +227,8 @@ def attention_rows(q_rows, rows, k, v, scale: float, causal: bool = False,
 
 def probs(q, k, scale: float, causal: bool = False):
     return _default().probs(q, k, scale, causal)
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool = False,
+                  nthreads: int = 0):
+    return _default().attention_bwd(q, k, v, dout, scale, causal, nthreads)

@@ -269,3 +269,171 @@ int oracle_probs_f64(const double *q, const double *k, int64_t nq, int64_t nk,
     }
     return 0;
 }
+
+/* ==== gradients ======================================================
+ *
+ * The pages say that the method recomputes parts of the attention matrix in
+ * the backward pass instead of storing it (unite.ai page, section "Enter
+ * Flash Attention", the recomputation idea) and that FlashAttention-2 made
+ * that backward pass nearly as fast as the forward one (same page,
+ * "FlashAttention-2", second improvement).  They give no formula for it, so
+ * the reference is the plain definition: the exact gradient of the forward
+ * definition above with respect to Q, K and V, for an incoming gradient dO
+ * of O (the derivative of a loss L with dL/dO = dO).  Written out per head,
+ * with P the probability matrix of the forward pass:
+ *
+ *   dV_j  = sum_i P_ij dO_i                       (O_i = sum_j P_ij V_j)
+ *   dP_ij = dO_i . V_j
+ *   dS_ij = P_ij (dP_ij - D_i),  D_i = sum_j P_ij dP_ij
+ *                                  (Jacobian of the row softmax)
+ *   dQ_i  = scale * sum_j dS_ij K_j                (S_ij = scale Q_i . K_j)
+ *   dK_j  = scale * sum_i dS_ij Q_i
+ *
+ * Masked entries have P_ij = 0 and so contribute nothing.  Everything is in
+ * double precision, one query row at a time over all of its keys.  Rows are
+ * split statically over the threads; each thread sums its rows' dK and dV
+ * contributions privately and the partial sums are added in thread order,
+ * so a given thread count always gives the same bits.
+ */
+
+typedef struct {
+    const double *q, *k, *v, *dout;
+    double *dq, *delta;
+    double *dk_part, *dv_part; /* this thread's [nk][d] partial sums */
+    int64_t r0, r1, nk, d;
+    double scale;
+    int causal;
+    int failed;
+} bwd_job_t;
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job_t *jb = (bwd_job_t *)arg;
+    const int64_t nk = jb->nk, d = jb->d;
+    double *p = (double *)malloc(sizeof(double) * (size_t)nk);
+    double *dp = (double *)malloc(sizeof(double) * (size_t)nk);
+    if (!p || !dp) {
+        free(p);
+        free(dp);
+        jb->failed = 1;
+        return NULL;
+    }
+    memset(jb->dk_part, 0, sizeof(double) * (size_t)(nk * d));
+    memset(jb->dv_part, 0, sizeof(double) * (size_t)(nk * d));
+    for (int64_t i = jb->r0; i < jb->r1; ++i) {
+        const double *qi = jb->q + i * d;
+        const double *gi = jb->dout + i * d;
+        double m, l;
+        probs_row(qi, jb->k, nk, d, jb->scale, jb->causal, i, p, &m, &l);
+        /* dP_ij and D_i */
+        double di = 0.0;
+        for (int64_t j = 0; j < nk; ++j) {
+            const double *vj = jb->v + j * d;
+            double s = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                s += gi[c] * vj[c];
+            dp[j] = s;
+            di += p[j] * s;
+        }
+        if (jb->delta)
+            jb->delta[i] = di;
+        double *dqi = jb->dq + i * d;
+        for (int64_t c = 0; c < d; ++c)
+            dqi[c] = 0.0;
+        for (int64_t j = 0; j < nk; ++j) {
+            const double ds = p[j] * (dp[j] - di);
+            const double *kj = jb->k + j * d;
+            double *dkj = jb->dk_part + j * d;
+            double *dvj = jb->dv_part + j * d;
+            for (int64_t c = 0; c < d; ++c) {
+                dqi[c] += ds * kj[c];
+                dkj[c] += ds * qi[c];
+                dvj[c] += p[j] * gi[c];
+            }
+        }
+        for (int64_t c = 0; c < d; ++c)
+            dqi[c] *= jb->scale;
+    }
+    free(p);
+    free(dp);
+    return NULL;
+}
+
+/*
+ * Gradients of every head.
+ *   q, dout, dq: [nh][nq][d];  k, v, dk, dv: [nh][nk][d];
+ *   delta: [nh][nq] (D_i above) or NULL.
+ * Returns the number of threads used, or -1 on allocation failure / bad size.
+ */
+int oracle_attention_bwd_f64(const double *q, const double *k, const double *v,
+                             const double *dout, double *dq, double *dk,
+                             double *dv, double *delta, int64_t nh, int64_t nq,
+                             int64_t nk, int64_t d, double scale, int causal,
+                             int nthreads)
+{
+    if (nh < 0 || nq < 1 || nk < 1 || d < 1)
+        return -1;
+    if (nthreads <= 0)
+        nthreads = oracle_default_threads();
+    if (nthreads > nq)
+        nthreads = (int)nq;
+    const size_t part = (size_t)(nk * d);
+    double *parts = (double *)malloc(sizeof(double) * part * 2 * (size_t)nthreads);
+    bwd_job_t *jobs = (bwd_job_t *)calloc((size_t)nthreads, sizeof(bwd_job_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    int *started = (int *)calloc((size_t)nthreads, sizeof(int));
+    int rc = nthreads;
+    if (!parts || !jobs || !th || !started) {
+        rc = -1;
+        goto out;
+    }
+    for (int64_t h = 0; h < nh && rc > 0; ++h) {
+        for (int t = 0; t < nthreads; ++t) {
+            bwd_job_t *jb = &jobs[t];
+            jb->q = q + h * nq * d;
+            jb->dout = dout + h * nq * d;
+            jb->k = k + h * nk * d;
+            jb->v = v + h * nk * d;
+            jb->dq = dq + h * nq * d;
+            jb->delta = delta ? delta + h * nq : NULL;
+            jb->dk_part = parts + (size_t)(2 * t) * part;
+            jb->dv_part = parts + (size_t)(2 * t + 1) * part;
+            jb->r0 = nq * t / nthreads;
+            jb->r1 = nq * (t + 1) / nthreads;
+            jb->nk = nk;
+            jb->d = d;
+            jb->scale = scale;
+            jb->causal = causal;
+            jb->failed = 0;
+            started[t] = 0;
+        }
+        for (int t = 1; t < nthreads; ++t)
+            started[t] = pthread_create(&th[t], NULL, bwd_worker, &jobs[t]) == 0;
+        bwd_worker(&jobs[0]);
+        for (int t = 1; t < nthreads; ++t) {
+            if (started[t])
+                pthread_join(th[t], NULL);
+            else
+                bwd_worker(&jobs[t]); /* could not start: run it here */
+        }
+        double *dkh = dk + h * nk * d, *dvh = dv + h * nk * d;
+        for (size_t e = 0; e < part; ++e) {
+            double sk = 0.0, sv = 0.0;
+            for (int t = 0; t < nthreads; ++t) {
+                sk += parts[(size_t)(2 * t) * part + e];
+                sv += parts[(size_t)(2 * t + 1) * part + e];
+            }
+            dkh[e] = scale * sk;
+            dvh[e] = sv;
+        }
+        for (int t = 0; t < nthreads; ++t)
+            if (jobs[t].failed)
+                rc = -1;
+    }
+out:
+    free(parts);
+    free(jobs);
+    free(th);
+    free(started);
+    return rc;
+}

@@ -292,6 +292,142 @@ def pin_rows_match_full(orc):
         _close(lrow, lse[0, rows], tol=0, what="rows lse")
 
 
+# ---------------------------------------------------------------------------
+# gradients
+
+
+def _loss(orc, q, k, v, g, scale, causal):
+    """L = sum(O * g): its gradient with respect to O is g."""
+    o, _, _ = orc.attention(q, k, v, scale, causal)
+    return float(np.sum(o * g))
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient entry matches the central difference of the forward
+    oracle's loss sum(O * dO): d/dx is read off the forward definition by
+    perturbing x, independently of how the gradient formula is written."""
+    r = _rng(20)
+    h = 1e-5
+    for nh, nq, nk, d, scale, causal in ((1, 5, 5, 3, 0.8, False),
+                                         (2, 4, 4, 3, -1.1, True),
+                                         (1, 3, 6, 2, 0.5, False),
+                                         (1, 1, 1, 2, 0.9, False),
+                                         (1, 6, 6, 4, 1.3, True)):
+        q = r.standard_normal((nh, nq, d))
+        k = r.standard_normal((nh, nk, d))
+        v = r.standard_normal((nh, nk, d))
+        g = r.standard_normal((nh, nq, d))
+        dq, dk, dv, _, _ = orc.attention_bwd(q, k, v, g, scale, causal)
+        for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.empty_like(x)
+            for idx in np.ndindex(x.shape):
+                x0 = x[idx]
+                x[idx] = x0 + h
+                lp = _loss(orc, q, k, v, g, scale, causal)
+                x[idx] = x0 - h
+                lm = _loss(orc, q, k, v, g, scale, causal)
+                x[idx] = x0
+                num[idx] = (lp - lm) / (2 * h)
+            _close(grad, num, tol=1e-7, what="d%s finite differences %s"
+                   % (name, (nh, nq, nk, d, scale, causal)))
+
+
+def pin_bwd_sums(orc):
+    """Rows of P sum to one, so sum_j dV_j = sum_i dO_i; the softmax is
+    unchanged by a common shift of a row's logits, so sum_j dS_ij = 0 and
+    sum_j dK_j = 0."""
+    r = _rng(21)
+    for causal in (False, True):
+        q = r.standard_normal((2, 40, 8))
+        k = r.standard_normal((2, 40, 8)) * 2
+        v = r.standard_normal((2, 40, 8))
+        g = r.standard_normal((2, 40, 8))
+        _, dk, dv, _, _ = orc.attention_bwd(q, k, v, g, 0.6, causal)
+        _close(dv.sum(axis=1), g.sum(axis=1), what="sum dV")
+        _close(dk.sum(axis=1), np.zeros((2, 8)), what="sum dK")
+
+
+def pin_bwd_constant_v(orc):
+    """All value rows equal: O does not depend on Q or K, so dQ = dK = 0."""
+    r = _rng(22)
+    for causal in (False, True):
+        q = r.standard_normal((1, 30, 6))
+        k = r.standard_normal((1, 30, 6))
+        v = np.tile(r.standard_normal((1, 1, 6)), (1, 30, 1))
+        g = r.standard_normal((1, 30, 6))
+        dq, dk, _, _, _ = orc.attention_bwd(q, k, v, g, 0.9, causal)
+        _close(dq, np.zeros_like(dq), what="dQ constant V")
+        _close(dk, np.zeros_like(dk), what="dK constant V")
+
+
+def pin_bwd_zero_scale(orc):
+    """scale = 0: uniform attention over the visible keys; dQ = dK = 0 and
+    dV_j = sum over the rows i that see key j of dO_i / (number of keys row
+    i sees) -- 1/N for every row without a mask, 1/(i+1) with it."""
+    r = _rng(23)
+    n, d = 12, 5
+    q = r.standard_normal((1, n, d))
+    k = r.standard_normal((1, n, d))
+    v = r.standard_normal((1, n, d))
+    g = r.standard_normal((1, n, d))
+    for causal in (False, True):
+        dq, dk, dv, _, _ = orc.attention_bwd(q, k, v, g, 0.0, causal)
+        _close(dq, np.zeros_like(dq), what="dQ scale 0")
+        _close(dk, np.zeros_like(dk), what="dK scale 0")
+        want = np.zeros((n, d))
+        for j in range(n):
+            for i in range(n):
+                if causal and j > i:
+                    continue
+                want[j] += g[0, i] / ((i + 1) if causal else n)
+        _close(dv[0], want, what="dV scale 0")
+
+
+def pin_bwd_delta_is_dout_dot_o(orc):
+    """D_i = sum_j P_ij dP_ij equals dO_i . O_i because O_i = sum_j P_ij V_j
+    (the identity a tiled backward uses to get D without P)."""
+    r = _rng(24)
+    for causal in (False, True):
+        q = r.standard_normal((2, 25, 7))
+        k = r.standard_normal((2, 25, 7))
+        v = r.standard_normal((2, 25, 7))
+        g = r.standard_normal((2, 25, 7))
+        o, _, _ = orc.attention(q, k, v, 0.4, causal)
+        _, _, _, delta, _ = orc.attention_bwd(q, k, v, g, 0.4, causal)
+        _close(delta, np.sum(g * o, axis=-1), what="delta")
+
+
+def pin_bwd_causal_first_row_and_single_key(orc):
+    """Causal row 0 sees one key, so its P is the constant 1 and dQ_0 = 0;
+    with a single key everywhere, dV_0 = sum_i dO_i and dQ = dK = 0."""
+    r = _rng(25)
+    q = r.standard_normal((1, 9, 4))
+    k = r.standard_normal((1, 9, 4))
+    v = r.standard_normal((1, 9, 4))
+    g = r.standard_normal((1, 9, 4))
+    dq, _, _, _, _ = orc.attention_bwd(q, k, v, g, 0.7, True)
+    _close(dq[0, 0], np.zeros(4), what="causal dQ row 0")
+    dq, dk, dv, _, _ = orc.attention_bwd(q, k[:, :1], v[:, :1], g, 0.7, False)
+    _close(dv[0, 0], g[0].sum(axis=0), what="single key dV")
+    _close(dq, np.zeros_like(dq), what="single key dQ")
+    _close(dk, np.zeros_like(dk), what="single key dK")
+
+
+def pin_bwd_linear_in_dout(orc):
+    """The gradients are linear in the incoming gradient dO."""
+    r = _rng(26)
+    q = r.standard_normal((1, 20, 6))
+    k = r.standard_normal((1, 20, 6))
+    v = r.standard_normal((1, 20, 6))
+    g1 = r.standard_normal((1, 20, 6))
+    g2 = r.standard_normal((1, 20, 6))
+    a = orc.attention_bwd(q, k, v, g1, 0.5, True)
+    b = orc.attention_bwd(q, k, v, g2, 0.5, True)
+    c = orc.attention_bwd(q, k, v, g1 + 2 * g2, 0.5, True)
+    for i, name in enumerate(("dq", "dk", "dv")):
+        _close(c[i], a[i] + 2 * b[i], what="linearity " + name)
+
+
 ALL_PINS = [
     pin_rows_sum_to_one,
     pin_probs_closed_form_two_keys,
@@ -305,4 +441,11 @@ ALL_PINS = [
     pin_online_merge,
     pin_brute_force,
     pin_rows_match_full,
+    pin_bwd_finite_differences,
+    pin_bwd_sums,
+    pin_bwd_constant_v,
+    pin_bwd_zero_scale,
+    pin_bwd_delta_is_dout_dot_o,
+    pin_bwd_causal_first_row_and_single_key,
+    pin_bwd_linear_in_dout,
 ]

@@ -33,6 +33,19 @@ MUTANTS = [
     ("PV sum stops one key early", "int64_t jend = (causal && i + 1 < nk) ? i + 1 : nk;",
      "int64_t jend = (causal && i + 1 < nk) ? i : nk - 1;"),
     ("max taken as min", "if (p[j] > m)", "if (p[j] < m && p[j] > -INFINITY)"),
+    # gradients
+    ("dS without the D term", "p[j] * (dp[j] - di)", "p[j] * dp[j]"),
+    ("dS sign flipped", "p[j] * (dp[j] - di)", "p[j] * (di - dp[j])"),
+    ("dK accumulates K instead of Q", "dkj[c] += ds * qi[c];", "dkj[c] += ds * kj[c];"),
+    ("dV accumulates dS instead of P", "dvj[c] += p[j] * gi[c];", "dvj[c] += ds * gi[c];"),
+    ("dQ without the scale", "dqi[c] *= jb->scale;", "dqi[c] *= 1.0;"),
+    ("dK without the scale", "dkh[e] = scale * sk;", "dkh[e] = sk;"),
+    ("dP from K instead of V", "const double *vj = jb->v + j * d;",
+     "const double *vj = jb->k + j * d;"),
+    ("D summed without P", "di += p[j] * s;", "di += s;"),
+    ("partial sums of other threads dropped",
+     "for (int t = 0; t < nthreads; ++t) {\n                sk",
+     "for (int t = 0; t < 1; ++t) {\n                sk"),
 ]
 
 

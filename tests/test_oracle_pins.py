@@ -29,6 +29,21 @@ def test_thread_count_does_not_change_bits(orc):
     assert np.array_equal(o1, o8) and np.array_equal(l1, l8)
 
 
+def test_bwd_threads_repeatable(orc):
+    """The gradient oracle gives the same bits for the same thread count, and
+    agrees to rounding across thread counts (only the order in which the
+    per-thread dK/dV partial sums are added changes)."""
+    r = np.random.default_rng(5)
+    q, k, v, g = (r.standard_normal((2, 77, 16)) for _ in range(4))
+    a = orc.attention_bwd(q, k, v, g, 0.3, True, nthreads=3)
+    b = orc.attention_bwd(q, k, v, g, 0.3, True, nthreads=3)
+    c = orc.attention_bwd(q, k, v, g, 0.3, True, nthreads=1)
+    for i in range(4):
+        assert np.array_equal(a[i], b[i])
+        assert np.allclose(a[i], c[i], rtol=0, atol=1e-13)
+    assert a[4] == 3 and c[4] == 1
+
+
 def test_merge_reading_o2_unnormalised(orc):
     """The online-softmax section's O update weights the new block by
     e^(m2-m)/l without an l2 factor; that is only consistent if the new
