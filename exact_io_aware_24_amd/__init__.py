@@ -1,5 +1,5 @@
-"""MI355X-native exact attention forward (FlashAttention-2 order) -- Python
-binding of the C-ABI library ``libfa2.so`` (declared in ``include/fa2.h``).
+"""MI355X-native exact attention (FlashAttention-2 order), forward and
+backward -- Python binding of the C-ABI library ``libfa2.so`` (declared in ``include/fa2.h``).
 
 This module only marshals arguments: it checks tensor device/dtype/shape,
 passes raw device pointers and torch's current HIP stream to the library, and
@@ -30,8 +30,8 @@ FA2_ERR_ALIAS = -6
 FA2_ERR_HIP = -7
 
 # Every symbol include/fa2.h declares.
-EXPORTED = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_fp32", "fa2_strerror",
-            "fa2_version")
+EXPORTED = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_fp32", "fa2_bwd", "fa2_bwd_o32",
+            "fa2_strerror", "fa2_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -61,6 +61,11 @@ def lib() -> ctypes.CDLL:
         for name in ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_fp32"):
             f = getattr(L, name)
             f.argtypes = sig
+            f.restype = ctypes.c_int
+        bsig = [vp] * 10 + [i, i, i, i, ctypes.c_float, i, vp]
+        for name in ("fa2_bwd", "fa2_bwd_o32"):
+            f = getattr(L, name)
+            f.argtypes = bsig
             f.restype = ctypes.c_int
         L.fa2_strerror.argtypes = [i]
         L.fa2_strerror.restype = ctypes.c_char_p
@@ -159,3 +164,77 @@ def raw_call(fn: str, q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, scale,
     """Call an entry point with raw integer pointers; returns the code."""
     return int(getattr(lib(), fn)(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N,
                                   d, ctypes.c_float(scale), int(causal), stream))
+
+
+def backward(q, k, v, o, dout, lse, causal: bool = False,
+             scale: float | None = None, out_dtype=None, dq=None, dk=None,
+             dv=None, delta=None):
+    """Gradients of :func:`forward` with respect to ``q, k, v``.
+
+    ``q, k, v, o, dout``: contiguous bfloat16 GPU tensors ``[B, H, N, d]``
+    (the forward's inputs and output, and the gradient of the loss with
+    respect to ``o``); ``lse``: the forward's float32 ``[B, H, N]``.
+    ``causal`` and ``scale`` must be the forward's.  ``out_dtype``:
+    ``torch.bfloat16`` (default, ``fa2_bwd``) or ``torch.float32``
+    (``fa2_bwd_o32``).  ``dq, dk, dv`` and the float32 ``[B, H, N]``
+    workspace ``delta`` may be preallocated.  Returns ``(dq, dk, dv)``.
+    The kernels are enqueued on torch's current stream.
+    """
+    import torch
+    _check_tensors(q, k, v)
+    _check_tensors(o, dout, q)
+    if q.dtype != torch.bfloat16 or o.dtype != torch.bfloat16 \
+            or dout.dtype != torch.bfloat16:
+        raise ValueError("q, k, v, o and dout must be bfloat16")
+    B, H, N, d = (int(x) for x in q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    odt = torch.bfloat16 if out_dtype is None else out_dtype
+    if odt == torch.bfloat16:
+        fn = "fa2_bwd"
+    elif odt == torch.float32:
+        fn = "fa2_bwd_o32"
+    else:
+        raise ValueError("out_dtype must be bfloat16 or float32")
+
+    def vec(t, name):
+        if t is None:
+            return torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        if t.shape != (B, H, N) or t.dtype != torch.float32 \
+                or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("%s must be a contiguous float32 [B, H, N] tensor" % name)
+        return t
+
+    def grad(t, name):
+        if t is None:
+            return torch.empty((B, H, N, d), dtype=odt, device=q.device)
+        if t.shape != q.shape or t.dtype != odt or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError("%s must be a contiguous %s tensor shaped like q"
+                             % (name, odt))
+        return t
+
+    if lse is None:
+        raise ValueError("lse (from the forward pass) is required")
+    lse = vec(lse, "lse")
+    delta = vec(delta, "delta")
+    dq, dk, dv = grad(dq, "dq"), grad(dk, "dk"), grad(dv, "dv")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = getattr(lib(), fn)(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+            dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), B, H, N, d, ctypes.c_float(scale),
+            int(bool(causal)), stream)
+    if rc != FA2_OK:
+        raise FA2Error(rc, fn)
+    return dq, dk, dv
+
+
+def raw_call_bwd(fn: str, ptrs, B, H, N, d, scale, causal, stream=None) -> int:
+    """Call a backward entry point with ten raw integer pointers (q, k, v, o,
+    dout, lse, delta, dq, dk, dv); returns the code."""
+    if len(ptrs) != 10:
+        raise ValueError("ten pointers expected")
+    return int(getattr(lib(), fn)(*ptrs, B, H, N, d, ctypes.c_float(scale),
+                                  int(causal), stream))

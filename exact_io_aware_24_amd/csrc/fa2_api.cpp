@@ -81,6 +81,61 @@ fa2::FwdArgs make_args(const void *q, const void *k, const void *v, void *o,
   return a;
 }
 
+// Validation of the backward entry points: every pointer is required; the
+// four outputs (dq, dk, dv and the delta workspace) may overlap neither an
+// input nor each other.
+int validate_bwd(const void *q, const void *k, const void *v, const void *o,
+                 const void *dout, const float *lse, const float *delta,
+                 const void *dq, const void *dk, const void *dv, int B, int H,
+                 int N, int d, float scale, int out_bytes) {
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv)
+    return FA2_ERR_NULL;
+  // shape, head dimension, size limits and scale as for the forward
+  int rc = validate(q, k, v, o, nullptr, B, H, N, d, scale, 2, 2,
+                    fa2::kBf16BwdRowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc != FA2_OK && rc != FA2_ERR_ALIAS) return rc;
+  if (misaligned(dout) || misaligned(lse) || misaligned(delta) ||
+      misaligned(dq) || misaligned(dk) || misaligned(dv))
+    return FA2_ERR_ALIGN;
+  const int64_t elems = static_cast<int64_t>(B) * H * N * d;
+  const int64_t rows = static_cast<int64_t>(B) * H * N;
+  const Range in[6] = {span(q, elems * 2),    span(k, elems * 2),
+                       span(v, elems * 2),    span(o, elems * 2),
+                       span(dout, elems * 2), span(lse, rows * 4)};
+  const Range out[4] = {span(dq, elems * out_bytes), span(dk, elems * out_bytes),
+                        span(dv, elems * out_bytes), span(delta, rows * 4)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], in[j])) return FA2_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out[j])) return FA2_ERR_ALIAS;
+  }
+  return FA2_OK;
+}
+
+fa2::BwdArgs make_bwd_args(const void *q, const void *k, const void *v,
+                           const void *o, const void *dout, const float *lse,
+                           float *delta, void *dq, void *dk, void *dv, int B,
+                           int H, int N, int d, float scale, int causal) {
+  fa2::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.bh = B * H;
+  a.n = N;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  return a;
+}
+
 int finish(hipError_t e) { return e == hipSuccess ? FA2_OK : FA2_ERR_HIP; }
 
 }  // namespace
@@ -118,20 +173,47 @@ FA2_EXPORT int fa2_fwd_fp32(const float *q, const float *k, const float *v,
       static_cast<hipStream_t>(stream)));
 }
 
+FA2_EXPORT int fa2_bwd(const void *q, const void *k, const void *v,
+                       const void *o, const void *dout, const float *lse,
+                       float *delta, void *dq, void *dk, void *dv, int B, int H,
+                       int N, int d, float scale, int causal, void *stream) {
+  int rc = validate_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d,
+                        scale, 2);
+  if (rc != FA2_OK) return rc;
+  return finish(fa2::launch_bwd_bf16(
+      make_bwd_args(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale,
+                    causal),
+      false, static_cast<hipStream_t>(stream)));
+}
+
+FA2_EXPORT int fa2_bwd_o32(const void *q, const void *k, const void *v,
+                           const void *o, const void *dout, const float *lse,
+                           float *delta, float *dq, float *dk, float *dv, int B,
+                           int H, int N, int d, float scale, int causal,
+                           void *stream) {
+  int rc = validate_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d,
+                        scale, 4);
+  if (rc != FA2_OK) return rc;
+  return finish(fa2::launch_bwd_bf16(
+      make_bwd_args(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale,
+                    causal),
+      true, static_cast<hipStream_t>(stream)));
+}
+
 FA2_EXPORT const char *fa2_strerror(int code) {
   switch (code) {
     case FA2_OK: return "success";
-    case FA2_ERR_NULL: return "a required pointer (q, k, v or o) is NULL";
+    case FA2_ERR_NULL: return "a required pointer is NULL";
     case FA2_ERR_SHAPE:
       return "invalid shape: B, H and N must be >= 1 and the tensors within "
              "the supported size";
     case FA2_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
     case FA2_ERR_SCALE: return "scale is not finite";
     case FA2_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case FA2_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA2_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA2_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown fa2 error code";
   }
 }
 
-FA2_EXPORT int fa2_version(void) { return 1; }
+FA2_EXPORT int fa2_version(void) { return 2; }

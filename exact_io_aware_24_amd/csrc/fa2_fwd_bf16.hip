@@ -40,9 +40,9 @@
 //    the two half-waves, and the rescale factor is a per-lane scalar.
 //  * K and V go from HBM straight into LDS (buffer_load ... lds: no register
 //    staging), issued one tile ahead and double-buffered, one barrier per
-//    tile.  The loads are raw buffer loads with the per-head extent as the
-//    buffer size, so rows past the end of the sequence read as zero in
-//    hardware, with no branches.
+//    tile.  Each tile's loads go through a raw buffer descriptor that starts
+//    at the tile and ends at the end of the head, so rows past the end of
+//    the sequence read as zero in hardware, with no branches.
 //  * K is stored row-major with its 16-byte granules XOR-swizzled by the row,
 //    so the 16 lanes of each phase of a 128-bit read hit 16 distinct bank
 //    groups.  V is stored in blocks of 32 columns (each key's 64 bytes
@@ -63,26 +63,17 @@
 
 #include <type_traits>
 
+#include "fa2_device.h"
 #include "fa2_internal.h"
 
 namespace fa2 {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+using namespace dev;
 
 constexpr int kThreads = 256;
 constexpr int kRows = kBf16RowsPerBlock;  // 128 query rows per workgroup
-constexpr float kLn2 = 0.693147180559945309417f;
-constexpr float kLog2e = 1.442695040888963407360f;
 constexpr float kRescaleThreshold = 8.0f;  // base-2 units: P~ <= 256
-// Buffer descriptor word 3: 32-bit data format, raw (untyped) addressing.
-constexpr int kBufWord3 = 0x00020000;
 
 struct Params {
   const uint16_t *q, *k, *v;
@@ -114,73 +105,6 @@ __device__ __forceinline__ int kswz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
-// (x of lanes 0-31, x of lanes 32-63) as seen from every lane.
-__device__ __forceinline__ void halves(float x, float &lo, float &hi) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
-                                            __float_as_uint(x), false, false);
-  lo = __uint_as_float(r[0]);
-  hi = __uint_as_float(r[1]);
-}
-
-// Scheduling fence for LDS reads and MFMAs only: VALU, SALU, transcendental
-// and VMEM instructions may still be moved across it.  It pins operand
-// reads a whole MFMA group ahead of their consumers (the scheduler would
-// otherwise sink them to just before use, exposing LDS latency).
-__device__ __forceinline__ void pin_lds_mfma() {
-  __builtin_amdgcn_sched_barrier(0x0002 | 0x0004 | 0x0010 | 0x0020 | 0x0040 |
-                                 0x0200 | 0x0400);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) {
-  return __builtin_amdgcn_exp2f(x);
-}
-
-template <typename T>
-__device__ __forceinline__ T lds_load(const char *base, int byte_off) {
-  return *reinterpret_cast<const T *>(base + byte_off);
-}
-
-// Transposing LDS read: within each group of 16 lanes, lane L receives
-// element L % 4 of the 8-byte chunks addressed by lanes 4e + L / 4, e = 0..3.
-__device__ __forceinline__ s16x4 lds_read_tr(const char *base, int byte_off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4 *)(base + byte_off));
-}
-
-// 16 bytes per lane from a raw buffer straight into LDS at lds_addr + 16 *
-// lane (buffer_load_dwordx4 ... lds; M0 holds the wave-uniform LDS address).
-// Issued through asm so that the compiler does not track it: it would
-// otherwise wait for every such load before the next LDS read of ANY buffer,
-// serialising the prefetch.  The kernel itself waits (vmcnt(0)) before the
-// barrier that publishes a filled buffer, which is the only ordering needed.
-__device__ __forceinline__ void dma16(u32x4 rsrc, int voff, int soff,
-                                      uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
-      : "memory", "m0");
-}
-
-// Raw buffer descriptor (words 0-3) for `bytes` bytes at `base`, made
-// wave-uniform so that it lives in scalar registers.
-__device__ __forceinline__ u32x4 make_desc(const void *base, int bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  u32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
-  r[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32) & 0xffffu);
-  r[2] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bytes));
-  r[3] = static_cast<uint32_t>(kBufWord3);
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const char *p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const char *)(p)));
-}
-
 // Everything one wave needs while it walks the K/V tiles.
 template <int D>
 struct WaveState {
@@ -196,37 +120,39 @@ struct Offsets {
   int k_rd[Cfg<D>::NDT];  // K operand reads per 16-dim step
   int v_rd;               // V transposed reads (all others are immediates)
   int k_ld[4];            // K loads within a tile, one per wave load
-  int v_ld;               // V loads within a tile (wave load it at +it*VSTEP)
+  int v_ld[4];            // V loads within a tile, one per wave load
 };
 
-// The four 1 KB loads of K, and of V, that this wave issues for one tile.
+// The four 1 KB loads of K, and of V, that this wave issues for one tile
+// (bytes [tile_byte, ...) of the head; rows past its end load as zeros).
 // LDS destinations are wave-uniform (they go to M0).
 template <int D>
-__device__ __forceinline__ void issue_k(u32x4 rk,
+__device__ __forceinline__ void issue_k(const uint16_t *k, int head_bytes,
                                         const Offsets<D> &off, char *kbuf,
                                         int wv, int tile_byte) {
+  const u32x4 rk = tile_desc(k, head_bytes, tile_byte);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int inst = 4 * wv + it;
     const int vo = off.k_ld[it];
-    dma16(rk, vo, tile_byte, lds_addr(kbuf + inst * 1024));
+    dma16(rk, vo, 0, lds_addr(kbuf + inst * 1024));
   }
 }
 
 template <int D>
-__device__ __forceinline__ void issue_v(u32x4 rv,
+__device__ __forceinline__ void issue_v(const uint16_t *v, int head_bytes,
                                         const Offsets<D> &off, char *vbuf,
                                         int wv, int tile_byte) {
   using C = Cfg<D>;
+  const u32x4 rv = tile_desc(v, head_bytes, tile_byte);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     // d = 128: block of 32 columns = wave, 16-key group = it;
     // d = 64: block = wave / 2, 16-key group = 4 * (wave & 1) + it
     const int cg = (D == 128) ? wv : (wv >> 1);
     const int kb = (D == 128) ? it : (4 * (wv & 1) + it);
-    const int vo = off.v_ld;
-    const int so = tile_byte + it * 16 * D * 2;
-    dma16(rv, vo, so, lds_addr(vbuf + cg * C::BC * 64 + kb * 1024));
+    const int vo = off.v_ld[it];
+    dma16(rv, vo, 0, lds_addr(vbuf + cg * C::BC * 64 + kb * 1024));
   }
 }
 
@@ -382,10 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int hh = lane >> 5;  // half-wave
 
   // ---- workgroup -> (head, query block) ----------------------------------
-  const int w = blockIdx.x;
-  const int per_xcd = p.total >> 3;
-  int logical = w;
-  if (w < (per_xcd << 3)) logical = (w & 7) * per_xcd + (w >> 3);
+  const int logical = xcd_remap(blockIdx.x, p.total);
   const int bh = logical / p.n_qblocks;
   const int qbl = logical - bh * p.n_qblocks;
   const int qb = CAUSAL ? (p.n_qblocks - 1 - qbl) : qbl;
@@ -395,8 +318,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int head_bytes = N * D * 2;  // < 2^31 (host-validated)
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(p.q + head), 0, head_bytes, kBufWord3);
-  const u32x4 rk = make_desc(p.k + head, head_bytes);
-  const u32x4 rv = make_desc(p.v + head, head_bytes);
+  const uint16_t *kh = p.k + head;
+  const uint16_t *vh = p.v + head;
 
   const int q0 = qb * kRows;      // first query of the block
   const int qw = q0 + wv * 32;    // first query of this wave
@@ -422,7 +345,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   {
     const int cg = (D == 128) ? wv : (wv >> 1);
     const int kb0 = (D == 128) ? 0 : 4 * (wv & 1);
-    off.v_ld = (16 * kb0 + lane / 4) * D * 2 + (4 * cg + (lane & 3)) * 16;
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      off.v_ld[it] = (16 * (kb0 + it) + lane / 4) * D * 2 + (4 * cg + (lane & 3)) * 16;
   }
 
   // ---- Q into registers (B operand of S^T = K Q^T) -------------------------
@@ -475,11 +400,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   }
   // prologue: K(0), V(0) -> buffers 0; then K(1) in flight while S(0) is
   // computed.
-  issue_k<D>(rk, off, kbuf(0), wv, 0);
-  issue_v<D>(rv, off, vbuf(0), wv, 0);
+  issue_k<D>(kh, head_bytes, off, kbuf(0), wv, 0);
+  issue_v<D>(vh, head_bytes, off, vbuf(0), wv, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (ntiles > 1) issue_k<D>(rk, off, kbuf(1), wv, C::BC * D * 2);
+  if (ntiles > 1) issue_k<D>(kh, head_bytes, off, kbuf(1), wv, C::BC * D * 2);
   f32x16 sa[C::NKT], sb[C::NKT];
   scores<D>(kbuf(0), off, st.qreg, sa);
   if (n_full > 0)
@@ -494,8 +419,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
                   f32x16(&nxt)[C::NKT]) {
     constexpr int P = decltype(par_tag)::value;  // t & 1
     const int j0 = t * C::BC;
-    if (t + 2 < ntiles) issue_k<D>(rk, off, kbuf(P), wv, (j0 + 2 * C::BC) * D * 2);
-    issue_v<D>(rv, off, vbuf(1 - P), wv, (j0 + C::BC) * D * 2);
+    if (t + 2 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(P), wv, (j0 + 2 * C::BC) * D * 2);
+    issue_v<D>(vh, head_bytes, off, vbuf(1 - P), wv, (j0 + C::BC) * D * 2);
     scores<D>(kbuf(1 - P), off, st.qreg, nxt);
     bf16x8 pb[C::NKT][2];
     softmax_exp<D, false>(cur, st.m_run, c, pb, st.l_run);
@@ -522,8 +447,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   for (; t < ntiles; ++t) {
     const int j0 = t * C::BC;
     const int p = t & 1;
-    if (t + 2 < ntiles) issue_k<D>(rk, off, kbuf(p), wv, (j0 + 2 * C::BC) * D * 2);
-    if (t + 1 < ntiles) issue_v<D>(rv, off, vbuf(1 - p), wv, (j0 + C::BC) * D * 2);
+    if (t + 2 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(p), wv, (j0 + 2 * C::BC) * D * 2);
+    if (t + 1 < ntiles) issue_v<D>(vh, head_bytes, off, vbuf(1 - p), wv, (j0 + C::BC) * D * 2);
     if (t + 1 < w_tiles) scores<D>(kbuf(1 - p), off, st.qreg, sb);
     if (t < w_tiles) {
       const float mu = (st.m_run == -INFINITY) ? 0.f : st.m_run;

@@ -20,8 +20,24 @@ struct FwdArgs {
   bool causal;
 };
 
+// Arguments of the backward pass (device pointers, validated shapes).
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;  // [B*H][N][d] bf16
+  const float *lse;                  // [B*H][N]
+  float *delta;                      // [B*H][N], written
+  void *dq, *dk, *dv;                // [B*H][N][d], written
+  int bh;
+  int n;
+  int d;
+  float scale;
+  bool causal;
+};
+
 // bf16 q/k/v on MFMA; o is bf16 (o32 == false) or fp32 (o32 == true).
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s);
+
+// Gradients (bf16 MFMA); dq/dk/dv bf16 (o32 == false) or fp32 (true).
+hipError_t launch_bwd_bf16(const BwdArgs &a, bool o32, hipStream_t s);
 
 // fp32 q/k/v/o, fp32 arithmetic throughout.
 hipError_t launch_fwd_fp32(const FwdArgs &a, hipStream_t s);
@@ -29,5 +45,7 @@ hipError_t launch_fwd_fp32(const FwdArgs &a, hipStream_t s);
 // Query rows per workgroup of each kernel (the grid is B*H*ceil(N/rows)).
 constexpr int kBf16RowsPerBlock = 128;
 constexpr int kFp32RowsPerBlock = 64;
+// Rows (queries or keys) per workgroup of the backward kernels.
+constexpr int kBf16BwdRowsPerBlock = 128;
 
 }  // namespace fa2

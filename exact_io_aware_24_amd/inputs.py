@@ -94,6 +94,13 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16",
     return q, k, v
 
 
+def make_dout(B: int, H: int, N: int, d: int, seed: int = DEFAULT_SEED + 1):
+    """An incoming gradient of the output for the backward pass: bf16 CPU
+    tensor ``[B, H, N, d]`` of seeded standard normal values."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    return torch.randn(B, H, N, d, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
 def workload_inputs(w: Workload, seed: int = DEFAULT_SEED):
     """Inputs of a named workload (CPU tensors)."""
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed=seed,

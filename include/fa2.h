@@ -41,8 +41,9 @@
  * give bit-identical outputs on every call (no atomics, fixed reduction
  * order).
  *
- * Aliasing: q, k and v may alias one another (they are only read).  o and
- * lse must not overlap any input or each other (FA2_ERR_ALIAS).
+ * Aliasing: inputs may alias one another (they are only read).  Outputs (o
+ * and lse; dq, dk, dv and delta of the backward pass) must not overlap any
+ * input or each other (FA2_ERR_ALIAS).
  *
  * Errors: every argument is validated on the host before any HIP call, so a
  * rejected call has no effect and enqueues nothing.  A non-zero return is
@@ -56,12 +57,12 @@ extern "C" {
 #endif
 
 #define FA2_OK 0
-#define FA2_ERR_NULL (-1)    /* q, k, v or o is NULL                           */
+#define FA2_ERR_NULL (-1)    /* a required pointer is NULL                     */
 #define FA2_ERR_SHAPE (-2)   /* B, H or N < 1, or a size limit below exceeded */
 #define FA2_ERR_HEADDIM (-3) /* d is not 64 or 128                             */
 #define FA2_ERR_SCALE (-4)   /* scale is NaN or infinite                       */
 #define FA2_ERR_ALIGN (-5)   /* a pointer is not 16-byte aligned               */
-#define FA2_ERR_ALIAS (-6)   /* o or lse overlaps an input or each other       */
+#define FA2_ERR_ALIAS (-6)   /* an output overlaps an input or another output  */
 #define FA2_ERR_HIP (-7)     /* the kernel launch failed (hipGetLastError)     */
 
 /* Size limits (FA2_ERR_SHAPE beyond them): B*H*N*d <= FA2_MAX_ELEMS elements
@@ -108,10 +109,46 @@ int fa2_fwd_fp32(const float *q, const float *k, const float *v, float *o,
                  float *lse, int B, int H, int N, int d, float scale,
                  int causal, void *stream);
 
+/*
+ * fa2_bwd -- gradients of fa2_fwd with respect to q, k and v (bf16 in, bf16
+ * out), for the incoming gradient dout of o.
+ *   q, k, v : const bf16 [B][H][N][d], the forward inputs
+ *   o       : const bf16 [B][H][N][d], the forward output
+ *   dout    : const bf16 [B][H][N][d], gradient of the loss with respect to o
+ *   lse     : const float [B][H][N], the forward's log-sum-exp (required)
+ *   delta   : float [B][H][N], workspace owned by the caller; on completion it
+ *             holds D_i = sum_c dout_ic o_ic (fp32)
+ *   dq, dk, dv : bf16 [B][H][N][d], written (round-to-nearest-even)
+ *   B, H, N, d, scale, causal : as for fa2_fwd (the same values as the
+ *             forward call that produced o and lse)
+ * Computes the exact gradients of the forward definition,
+ *   P = exp(scale q k^T - lse) (masked entries 0),  dv = P^T dout,
+ *   dS = P * (dout v^T - D),  dq = scale dS k,  dk = scale dS^T q,
+ * recomputing P tile by tile from lse (no N x N buffer) -- the recomputation
+ * of the unite.ai page "Flash Attention: revolutionising transformer
+ * efficiency", section "Enter Flash Attention".  Three kernels are enqueued
+ * on `stream` in order (D, then dk/dv, then dq); no atomics, so results are
+ * bit-reproducible.  bf16 products, fp32 accumulation; P and dS are rounded
+ * to bf16 for the MFMA products.
+ */
+int fa2_bwd(const void *q, const void *k, const void *v, const void *o,
+            const void *dout, const float *lse, float *delta, void *dq,
+            void *dk, void *dv, int B, int H, int N, int d, float scale,
+            int causal, void *stream);
+
+/*
+ * fa2_bwd_o32 -- as fa2_bwd, but dq, dk, dv are float [B][H][N][d] (the
+ * same kernels without the final bf16 rounding).
+ */
+int fa2_bwd_o32(const void *q, const void *k, const void *v, const void *o,
+                const void *dout, const float *lse, float *delta, float *dq,
+                float *dk, float *dv, int B, int H, int N, int d, float scale,
+                int causal, void *stream);
+
 /* Static English description of a return code (never NULL). */
 const char *fa2_strerror(int code);
 
-/* Library ABI version: 1. */
+/* Library ABI version: 2 (1 had the forward entry points only). */
 int fa2_version(void);
 
 #ifdef __cplusplus

@@ -9,6 +9,20 @@ Tolerances (bf16 inputs; the benchmark spec's max-abs 1e-2 and rel-L2 5e-3):
   above; the literal max-abs is reported alongside;
 * lse: |lse - lse_ref| <= 1e-3 + 2e-6 |lse_ref|.
 fp32 inputs (fa2_fwd_fp32): max-abs <= 1e-5 on O and lse.
+
+Gradients (fa2_bwd / fa2_bwd_o32; no tolerance is stated anywhere for them):
+the bound is derived from a rounding model of the kernels' arithmetic --
+P and dS rounded to bf16 for their products, D = dO . O taken from the
+forward's bf16 output, fp32 accumulation, bf16 outputs -- evaluated against
+the fp64 oracle in ``test_bwd_tolerance_model.py``.  The model gives rel-L2
+<= 2.7e-3 and max|err| / max|ref| <= 4.5e-3 on standard normal inputs; with
+the 5 % x20 outlier rows, cancellation in dP - D amplifies the bf16 rounding
+of O to rel-L2 1.1e-2 and 3.6e-2 (dK).  The bounds below are ~3x those
+figures.  Gradients that vanish in exact arithmetic (a single key: dQ = dK
+= 0) are left with the fp32 rounding difference between the two equal ways
+of forming D (dO . O and sum_j P dP), so the relative measures use a floor
+of GRAD_FLOOR in their denominators (per element for max-abs, times
+sqrt(size) for the 2-norm).
 """
 import math
 
@@ -17,6 +31,30 @@ import numpy as np
 MAX_ABS = 1e-2
 REL_L2 = 5e-3
 FP32_ABS = 1e-5
+
+
+GRAD_REL_L2 = 8e-3
+GRAD_MAX_REL = 1.5e-2
+GRAD_FLOOR = 1e-3
+GRAD_REL_L2_HEAVY = 3e-2   # inputs with outlier rows
+GRAD_MAX_REL_HEAVY = 1e-1
+
+
+def compare_grad(g, g_ref, heavy=False):
+    """Error figures of one gradient tensor against the oracle's."""
+    g = np.asarray(g, dtype=np.float64)
+    g_ref = np.asarray(g_ref, dtype=np.float64)
+    assert g.shape == g_ref.shape, (g.shape, g_ref.shape)
+    finite = bool(np.all(np.isfinite(g)))
+    err = np.abs(g - g_ref)
+    ref_max = max(float(np.abs(g_ref).max()), GRAD_FLOOR)
+    max_rel = float(err.max()) / ref_max if err.size else 0.0
+    rel_l2 = float(np.linalg.norm(g - g_ref) /
+                   max(np.linalg.norm(g_ref), GRAD_FLOOR * math.sqrt(g.size)))
+    lim_l2, lim_max = ((GRAD_REL_L2_HEAVY, GRAD_MAX_REL_HEAVY) if heavy
+                       else (GRAD_REL_L2, GRAD_MAX_REL))
+    return dict(finite=finite, rel_l2=rel_l2, max_rel=max_rel,
+                ok=finite and rel_l2 <= lim_l2 and max_rel <= lim_max)
 
 
 def ulp_bf16(x):

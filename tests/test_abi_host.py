@@ -50,7 +50,7 @@ def test_codes_match_header():
 
 
 def test_version_and_strerror(L):
-    assert fa2.version() == 1
+    assert fa2.version() == 2
     seen = set()
     for name, code in header_codes().items():
         msg = fa2.strerror(code)
@@ -129,3 +129,58 @@ def test_binding_rejects_bad_tensors():
         fa2.forward(q[0], q[0], q[0])
     with pytest.raises(TypeError):
         fa2.forward(None, q, q)
+
+
+# Backward entry points: ten pointers (q, k, v, o, dout, lse, delta, dq, dk,
+# dv), all required.  Again only calls that validation rejects.
+BWD_FUNCS = ("fa2_bwd", "fa2_bwd_o32")
+BWD_NAMES = ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv")
+BWD_GOOD = {name: 0x10000000 + i * 64 * MiB for i, name in enumerate(BWD_NAMES)}
+BWD_SHAPE = dict(B=1, H=2, N=64, d=64, scale=0.125, causal=1)
+
+
+def call_bwd(fn, ptrs=None, **kw):
+    p = dict(BWD_GOOD)
+    p.update(ptrs or {})
+    a = dict(BWD_SHAPE)
+    a.update(kw)
+    return fa2.raw_call_bwd(fn, [p[n] for n in BWD_NAMES], a["B"], a["H"],
+                            a["N"], a["d"], a["scale"], a["causal"])
+
+
+@pytest.mark.parametrize("fn", BWD_FUNCS)
+def test_bwd_null_pointers(L, fn):
+    for name in BWD_NAMES:
+        assert call_bwd(fn, {name: None}) == fa2.FA2_ERR_NULL, name
+
+
+@pytest.mark.parametrize("fn", BWD_FUNCS)
+def test_bwd_bad_arguments(L, fn):
+    for kw in (dict(B=0), dict(H=0), dict(N=0), dict(N=1 << 30, d=128),
+               dict(B=1 << 16, H=1 << 16, N=1)):
+        assert call_bwd(fn, **kw) == fa2.FA2_ERR_SHAPE, kw
+    for d in (0, 32, 96, 256):
+        assert call_bwd(fn, d=d) == fa2.FA2_ERR_HEADDIM, d
+    for s in (float("nan"), float("inf")):
+        assert call_bwd(fn, scale=s) == fa2.FA2_ERR_SCALE
+    for name in BWD_NAMES:
+        assert call_bwd(fn, {name: BWD_GOOD[name] + 4}) == fa2.FA2_ERR_ALIGN, name
+
+
+@pytest.mark.parametrize("fn", BWD_FUNCS)
+def test_bwd_aliasing(L, fn):
+    # every output against every input, and the outputs against each other
+    outs = ("delta", "dq", "dk", "dv")
+    for o in outs:
+        for i in ("q", "k", "v", "o", "dout", "lse"):
+            assert call_bwd(fn, {o: BWD_GOOD[i] + 16}) == fa2.FA2_ERR_ALIAS, (o, i)
+        for o2 in outs:
+            if o2 != o:
+                assert call_bwd(fn, {o: BWD_GOOD[o2]}) == fa2.FA2_ERR_ALIAS, (o, o2)
+
+
+def test_bwd_binding_checks():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa2.backward(q, q, q, q, q, torch.zeros(1, 1, 8))
