@@ -6,7 +6,10 @@
 One step is one call of ``fa2_fwd`` (bf16 in, bf16 out, with lse) on the
 headline workload B=2, H=16, N=8192, d=128, causal, inputs resident in HBM
 (``--entry fa2_fwd_o32`` times the fp32-output sibling, ``--workload`` and
-``--seq-len`` pick another shape).
+``--seq-len`` pick another shape).  ``--pass bwd`` times ``fa2_bwd`` instead
+(gradients for a seeded dO, after one forward call that provides O and lse),
+counted at the usual 2.5x the forward's flop: the five products S, dP, dV,
+dK, dQ.
 W untimed warm-up steps are followed by exactly K timed steps between HIP
 events on the stream the kernel is launched on.  Rank 0 prints one JSON line:
 TFLOP/s (4*B*H*N^2*d, halved for causal), the roofline of the kernel against
@@ -37,7 +40,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_24_amd", "csrc", "fa2_fwd_bf16.hip")
+CSRC = os.path.join(ROOT, "exact_io_aware_24_amd", "csrc")
+KERNEL_SRCS = {"fwd": ("fa2_fwd_bf16.hip", "fa2_device.h"),
+               "bwd": ("fa2_bwd_bf16.hip", "fa2_device.h")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -53,17 +58,22 @@ def compulsory_bytes(B, H, N, d, in_bytes=2, out_bytes=2, lse=True) -> float:
     return 3 * n * in_bytes + n * out_bytes + (float(B) * H * N * 4 if lse else 0)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(which: str = "fwd") -> str:
+    """Hash of the kernel sources of one pass (names the kernel version that
+    a counter summary was taken on)."""
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS[which]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def read_traffic(workload_name: str):
+def read_traffic(workload_name: str, which: str = "fwd"):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading on
     a copy of known size), or None when there is none or it was taken on a
     different kernel source."""
-    path = os.path.join(PROFILES, "counters_fa2_fwd_bf16_%s.md" % workload_name)
+    path = os.path.join(PROFILES, "counters_fa2_%s_bf16_%s.md" % (which, workload_name))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -73,13 +83,39 @@ def read_traffic(workload_name: str):
             key, val = line[2:].split(":", 1)
             vals[key.strip()] = val.strip().strip("`")
     try:
-        if vals.get("kernel_source_sha256") != kernel_source_hash():
+        if vals.get("kernel_source_sha256") != kernel_source_hash(which):
             return None
         fetch = float(vals["fetch_bytes_per_launch"])
         write = float(vals["write_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
     return fetch + write
+
+
+def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
+    """Time the fp64 gradient oracle (as it stands) on whole heads of the
+    workload, as many as fit the budget after timing the first one."""
+    import oracle
+    BH = w.B * w.H
+    qf, kf, vf, gf = (t.reshape(BH, w.N, w.d) for t in (q, k, v, do))
+    n_heads, dt, threads = 0, 0.0, 0
+    t0 = time.perf_counter()
+    while n_heads < BH and (n_heads == 0 or dt * (n_heads + 1) / n_heads <= budget_s):
+        h = n_heads
+        _, _, _, _, threads = oracle.attention_bwd(qf[h], kf[h], vf[h], gf[h],
+                                                   w.scale, w.causal)
+        n_heads += 1
+        dt = time.perf_counter() - t0
+    flops = 2.5 * w.flops / BH * n_heads
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "%d of %d heads (all %d rows each) of %s, backward; fp64 C "
+                  "oracle, %.1f s wall, %.3g flop counted like the GPU metric"
+                  % (n_heads, BH, w.N, w.describe(), dt, flops),
+    }
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
@@ -132,8 +168,11 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--entry", default="fa2_fwd", choices=("fa2_fwd", "fa2_fwd_o32"),
-                    help="entry point to time (o32: fp32 output)")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=("fwd", "bwd"),
+                    help="forward (fa2_fwd) or backward (fa2_bwd) pass")
+    ap.add_argument("--entry", default=None,
+                    choices=("fa2_fwd", "fa2_fwd_o32", "fa2_bwd", "fa2_bwd_o32"),
+                    help="entry point to time (o32: fp32 outputs)")
     ap.add_argument("--seq-len", type=int, default=0,
                     help="override the workload's sequence length")
     ap.add_argument("--per-call", action="store_true",
@@ -170,16 +209,35 @@ def main(argv=None):
             print("--seq-len must be >= 1", file=sys.stderr)
             return 2
         w = dataclasses.replace(w, N=args.seq_len)
+    entry = args.entry or ("fa2_fwd" if args.which == "fwd" else "fa2_bwd")
+    if not entry.startswith("fa2_" + args.which):
+        print("--entry %s does not belong to --pass %s" % (entry, args.which),
+              file=sys.stderr)
+        return 2
     dev = torch.device("cuda:0")
     q, k, v = wl.make_inputs(w.B, w.H, w.N, w.d, w.dtype, outliers=w.outliers)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    out_dtype = torch.float32 if args.entry == "fa2_fwd_o32" else torch.bfloat16
-    o = torch.empty(qd.shape, dtype=out_dtype, device=dev)
+    out_dtype = torch.float32 if entry.endswith("_o32") else torch.bfloat16
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    if args.which == "fwd":
+        flops = w.flops
+        o = torch.empty(qd.shape, dtype=out_dtype, device=dev)
 
-    def step():
-        fa2.forward(qd, kd, vd, causal=w.causal, scale=w.scale,
-                    out_dtype=out_dtype, out=o, lse=lse)
+        def step():
+            fa2.forward(qd, kd, vd, causal=w.causal, scale=w.scale,
+                        out_dtype=out_dtype, out=o, lse=lse)
+    else:
+        flops = 2.5 * w.flops
+        do = wl.make_dout(w.B, w.H, w.N, w.d)
+        dod = do.to(dev)
+        o, _ = fa2.forward(qd, kd, vd, causal=w.causal, scale=w.scale, lse=lse)
+        grads = [torch.empty(qd.shape, dtype=out_dtype, device=dev) for _ in range(3)]
+        delta = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+
+        def step():
+            fa2.backward(qd, kd, vd, o, dod, lse, causal=w.causal, scale=w.scale,
+                         out_dtype=out_dtype, dq=grads[0], dk=grads[1],
+                         dv=grads[2], delta=delta)
 
     for _ in range(args.warmup):
         step()
@@ -198,7 +256,7 @@ def main(argv=None):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    tflops = w.flops / (ms * 1e-3) / 1e12
+    tflops = flops / (ms * 1e-3) / 1e12
 
     per_call = None
     if args.per_call:
@@ -218,13 +276,13 @@ def main(argv=None):
         per = sorted(a.elapsed_time(b) for a, b in pairs)
         per_call = {"median_ms": round(per[len(per) // 2], 5),
                     "min_ms": round(per[0], 5),
-                    "median_tflops": round(w.flops / (per[len(per) // 2] * 1e-3) / 1e12, 3),
+                    "median_tflops": round(flops / (per[len(per) // 2] * 1e-3) / 1e12, 3),
                     "cold_mall_mib": args.cold_mall}
 
-    same_shape = not args.seq_len and args.entry == "fa2_fwd"
-    traffic = read_traffic(name) if same_shape else None
+    same_shape = not args.seq_len and entry == "fa2_" + args.which
+    traffic = read_traffic(name, args.which) if same_shape else None
     rec = {
-        "metric": "attention fwd TFLOP/s (1 MI355X) and % of bf16 MFMA peak",
+        "metric": "attention %s TFLOP/s (1 MI355X) and %% of bf16 MFMA peak" % args.which,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -238,7 +296,7 @@ def main(argv=None):
         "data": "synthetic (seeded randn, bf16)",
         "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale,
-                   "flops_per_step": w.flops, "entry_point": args.entry},
+                   "flops_per_step": flops, "entry_point": entry},
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 3),
@@ -250,13 +308,15 @@ def main(argv=None):
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "score_matrix_bytes_not_written": score_matrix_bytes(w.B, w.H, w.N),
         "compulsory_hbm_bytes": compulsory_bytes(w.B, w.H, w.N, w.d),
-        "kernel_source_sha256": kernel_source_hash(),
+        "kernel_source_sha256": kernel_source_hash(args.which),
         "gpu": torch.cuda.get_device_name(dev),
     }
     if per_call is not None:
         rec["per_call"] = per_call
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        rec["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_budget)
+                               if args.which == "fwd" else
+                               cpu_baseline_bwd(w, q, k, v, do, args.cpu_budget))
     print(json.dumps(rec), flush=True)
     return 0
 

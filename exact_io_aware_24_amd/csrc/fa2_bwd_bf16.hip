@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t *o,
 // the sequence end read as 0, which gives them zero weight because their
 // Q and dO rows are zero too).
 template <int D, bool CAUSAL, bool O32>
-__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
   using C = BCfg<D>;
   // [Q 0][Q 1][dO 0][dO 1][lse 0][lse 1][D 0][D 1] (statistics: 1 KB each,
   // of which the first 256 bytes are used)
