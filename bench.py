@@ -123,8 +123,12 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     workload: whole heads, all their rows, as many heads as fit the budget
     after a one-head calibration on a row subset."""
     import numpy as np
+    import torch
     import oracle
     BH = w.B * w.H
+    if w.kv_heads != w.H:  # grouped K/V heads: the oracle's definition
+        k = torch.from_numpy(oracle.expand_kv_heads(k, w.H))
+        v = torch.from_numpy(oracle.expand_kv_heads(v, w.H))
     qf, kf, vf = (t.reshape(BH, w.N, w.d) for t in (q, k, v))
 
     def head_flops(rows):
@@ -215,7 +219,11 @@ def main(argv=None):
               file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
-    q, k, v = wl.make_inputs(w.B, w.H, w.N, w.d, w.dtype, outliers=w.outliers)
+    if args.which == "bwd" and w.kv_heads != w.H:
+        print("the backward pass takes one K/V head per query head", file=sys.stderr)
+        return 2
+    q, k, v = wl.make_inputs(w.B, w.H, w.N, w.d, w.dtype, outliers=w.outliers,
+                             H_kv=w.H_kv)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     out_dtype = torch.float32 if entry.endswith("_o32") else torch.bfloat16
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)

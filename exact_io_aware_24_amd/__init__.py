@@ -30,8 +30,9 @@ FA2_ERR_ALIAS = -6
 FA2_ERR_HIP = -7
 
 # Every symbol include/fa2.h declares.
-EXPORTED = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_fp32", "fa2_bwd", "fa2_bwd_o32",
-            "fa2_strerror", "fa2_version")
+EXPORTED = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_gqa", "fa2_fwd_gqa_o32",
+            "fa2_fwd_fp32", "fa2_bwd", "fa2_bwd_o32", "fa2_strerror",
+            "fa2_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -62,6 +63,11 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = sig
             f.restype = ctypes.c_int
+        gsig = [vp, vp, vp, vp, vp, i, i, i, i, i, ctypes.c_float, i, vp]
+        for name in ("fa2_fwd_gqa", "fa2_fwd_gqa_o32"):
+            f = getattr(L, name)
+            f.argtypes = gsig
+            f.restype = ctypes.c_int
         bsig = [vp] * 10 + [i, i, i, i, ctypes.c_float, i, vp]
         for name in ("fa2_bwd", "fa2_bwd_o32"):
             f = getattr(L, name)
@@ -83,7 +89,9 @@ def version() -> int:
     return int(lib().fa2_version())
 
 
-def _check_tensors(q, k, v):
+def _check_tensors(q, k, v, grouped=False):
+    """Device, layout and dtype checks.  ``grouped``: k and v may have fewer
+    heads than q, a divisor of q's head count."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
@@ -94,8 +102,12 @@ def _check_tensors(q, k, v):
             raise ValueError("%s must be a GPU tensor" % name)
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError("q, k, v shapes differ: %s %s %s"
+    same = q.shape == k.shape == v.shape
+    grouped_ok = (grouped and k.shape == v.shape and k.shape[0] == q.shape[0]
+                  and k.shape[2:] == q.shape[2:] and k.shape[1] >= 1
+                  and q.shape[1] % k.shape[1] == 0)
+    if not (same or grouped_ok):
+        raise ValueError("q, k, v shapes do not match: %s %s %s"
                          % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v dtypes differ")
@@ -110,7 +122,10 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
     """Exact attention forward: ``softmax(scale * q k^T [+ causal mask]) v``.
 
     ``q, k, v``: contiguous GPU tensors ``[B, H, N, d]``, d in {64, 128},
-    all bfloat16 (MFMA path) or all float32 (fp32 path).
+    all bfloat16 (MFMA path) or all float32 (fp32 path).  With bfloat16
+    inputs ``k`` and ``v`` may be ``[B, H_kv, N, d]`` with H_kv dividing H
+    (grouped-query attention, ``fa2_fwd_gqa[_o32]``): query head h uses
+    key/value head ``h // (H // H_kv)``.
     ``out_dtype``: for bf16 inputs, ``torch.bfloat16`` (default, entry point
     ``fa2_fwd``) or ``torch.float32`` (``fa2_fwd_o32``); float32 inputs give
     float32 output (``fa2_fwd_fp32``).  ``scale`` defaults to ``1/sqrt(d)``.
@@ -119,10 +134,13 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
     The kernel is enqueued on torch's current stream.
     """
     import torch
-    _check_tensors(q, k, v)
+    _check_tensors(q, k, v, grouped=True)
     B, H, N, d = (int(x) for x in q.shape)
+    H_kv = int(k.shape[1])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if H_kv != H and q.dtype != torch.bfloat16:
+        raise ValueError("grouped K/V heads need bfloat16 inputs")
     if q.dtype == torch.float32:
         if out_dtype not in (None, torch.float32):
             raise ValueError("float32 inputs give float32 output")
@@ -135,6 +153,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
             fn = "fa2_fwd_o32"
         else:
             raise ValueError("out_dtype must be bfloat16 or float32")
+        if H_kv != H:
+            fn = fn.replace("fa2_fwd", "fa2_fwd_gqa")
     if out is None:
         out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
     elif out.shape != q.shape or out.dtype != odt or not out.is_contiguous() \
@@ -148,21 +168,24 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
             raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     else:
         lse = None
+    heads = (B, H, H_kv) if H_kv != H else (B, H)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = getattr(lib(), fn)(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
             lse.data_ptr() if lse is not None else None,
-            B, H, N, d, ctypes.c_float(scale), int(bool(causal)), stream)
+            *heads, N, d, ctypes.c_float(scale), int(bool(causal)), stream)
     if rc != FA2_OK:
         raise FA2Error(rc, fn)
     return out, lse
 
 
 def raw_call(fn: str, q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, scale,
-             causal, stream=None) -> int:
-    """Call an entry point with raw integer pointers; returns the code."""
-    return int(getattr(lib(), fn)(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N,
+             causal, stream=None, H_kv=None) -> int:
+    """Call a forward entry point with raw integer pointers; returns the
+    code.  ``H_kv`` is passed only to the grouped (``_gqa``) entry points."""
+    heads = (B, H) if H_kv is None else (B, H, H_kv)
+    return int(getattr(lib(), fn)(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, *heads, N,
                                   d, ctypes.c_float(scale), int(causal), stream))
 
 

@@ -33,11 +33,11 @@ bool misaligned(const void *p) {
 // addresses one head with 32-bit byte offsets, including one tile of reads
 // past the end that the hardware bounds check turns into zeros).
 int validate(const void *q, const void *k, const void *v, const void *o,
-             const float *lse, int B, int H, int N, int d, float scale,
-             int in_bytes, int out_bytes, int rows_per_block,
+             const float *lse, int B, int H, int H_kv, int N, int d,
+             float scale, int in_bytes, int out_bytes, int rows_per_block,
              int64_t max_per_head) {
   if (!q || !k || !v || !o) return FA2_ERR_NULL;
-  if (B < 1 || H < 1 || N < 1) return FA2_ERR_SHAPE;
+  if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H % H_kv != 0) return FA2_ERR_SHAPE;
   if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
   const int64_t bh = static_cast<int64_t>(B) * H;
   const int64_t per_head = static_cast<int64_t>(N) * d;
@@ -51,8 +51,9 @@ int validate(const void *q, const void *k, const void *v, const void *o,
       (lse && misaligned(lse)))
     return FA2_ERR_ALIGN;
   const int64_t elems = bh * per_head;
-  const Range rq = span(q, elems * in_bytes), rk = span(k, elems * in_bytes),
-              rv = span(v, elems * in_bytes), ro = span(o, elems * out_bytes);
+  const int64_t kv_elems = static_cast<int64_t>(B) * H_kv * per_head;
+  const Range rq = span(q, elems * in_bytes), rk = span(k, kv_elems * in_bytes),
+              rv = span(v, kv_elems * in_bytes), ro = span(o, elems * out_bytes);
   if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv))
     return FA2_ERR_ALIAS;
   if (lse) {
@@ -65,8 +66,8 @@ int validate(const void *q, const void *k, const void *v, const void *o,
 }
 
 fa2::FwdArgs make_args(const void *q, const void *k, const void *v, void *o,
-                       float *lse, int B, int H, int N, int d, float scale,
-                       int causal) {
+                       float *lse, int B, int H, int H_kv, int N, int d,
+                       float scale, int causal) {
   fa2::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -74,6 +75,8 @@ fa2::FwdArgs make_args(const void *q, const void *k, const void *v, void *o,
   a.o = o;
   a.lse = lse;
   a.bh = B * H;
+  a.h = H;
+  a.group = H / H_kv;
   a.n = N;
   a.d = d;
   a.scale = scale;
@@ -91,7 +94,7 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o,
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv)
     return FA2_ERR_NULL;
   // shape, head dimension, size limits and scale as for the forward
-  int rc = validate(q, k, v, o, nullptr, B, H, N, d, scale, 2, 2,
+  int rc = validate(q, k, v, o, nullptr, B, H, H, N, d, scale, 2, 2,
                     fa2::kBf16BwdRowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK && rc != FA2_ERR_ALIAS) return rc;
   if (misaligned(dout) || misaligned(lse) || misaligned(delta) ||
@@ -143,33 +146,56 @@ int finish(hipError_t e) { return e == hipSuccess ? FA2_OK : FA2_ERR_HIP; }
 FA2_EXPORT int fa2_fwd(const void *q, const void *k, const void *v, void *o,
                        float *lse, int B, int H, int N, int d, float scale,
                        int causal, void *stream) {
-  int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2, 2,
+  int rc = validate(q, k, v, o, lse, B, H, H, N, d, scale, 2, 2,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
-      make_args(q, k, v, o, lse, B, H, N, d, scale, causal), false,
+      make_args(q, k, v, o, lse, B, H, H, N, d, scale, causal), false,
+      static_cast<hipStream_t>(stream)));
+}
+
+FA2_EXPORT int fa2_fwd_gqa(const void *q, const void *k, const void *v,
+                           void *o, float *lse, int B, int H, int H_kv, int N,
+                           int d, float scale, int causal, void *stream) {
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, N, d, scale, 2, 2,
+                    fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc != FA2_OK) return rc;
+  return finish(fa2::launch_fwd_bf16(
+      make_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal), false,
+      static_cast<hipStream_t>(stream)));
+}
+
+FA2_EXPORT int fa2_fwd_gqa_o32(const void *q, const void *k, const void *v,
+                               float *o, float *lse, int B, int H, int H_kv,
+                               int N, int d, float scale, int causal,
+                               void *stream) {
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, N, d, scale, 2, 4,
+                    fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc != FA2_OK) return rc;
+  return finish(fa2::launch_fwd_bf16(
+      make_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal), true,
       static_cast<hipStream_t>(stream)));
 }
 
 FA2_EXPORT int fa2_fwd_o32(const void *q, const void *k, const void *v,
                            float *o, float *lse, int B, int H, int N, int d,
                            float scale, int causal, void *stream) {
-  int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 2, 4,
+  int rc = validate(q, k, v, o, lse, B, H, H, N, d, scale, 2, 4,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
-      make_args(q, k, v, o, lse, B, H, N, d, scale, causal), true,
+      make_args(q, k, v, o, lse, B, H, H, N, d, scale, causal), true,
       static_cast<hipStream_t>(stream)));
 }
 
 FA2_EXPORT int fa2_fwd_fp32(const float *q, const float *k, const float *v,
                             float *o, float *lse, int B, int H, int N, int d,
                             float scale, int causal, void *stream) {
-  int rc = validate(q, k, v, o, lse, B, H, N, d, scale, 4, 4,
+  int rc = validate(q, k, v, o, lse, B, H, H, N, d, scale, 4, 4,
                     fa2::kFp32RowsPerBlock, INT32_MAX);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_fp32(
-      make_args(q, k, v, o, lse, B, H, N, d, scale, causal),
+      make_args(q, k, v, o, lse, B, H, H, N, d, scale, causal),
       static_cast<hipStream_t>(stream)));
 }
 
@@ -205,8 +231,8 @@ FA2_EXPORT const char *fa2_strerror(int code) {
     case FA2_OK: return "success";
     case FA2_ERR_NULL: return "a required pointer is NULL";
     case FA2_ERR_SHAPE:
-      return "invalid shape: B, H and N must be >= 1 and the tensors within "
-             "the supported size";
+      return "invalid shape: B, H, N >= 1, H_kv >= 1 dividing H, and the "
+             "tensors within the supported size";
     case FA2_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
     case FA2_ERR_SCALE: return "scale is not finite";
     case FA2_ERR_ALIGN: return "a pointer is not 16-byte aligned";
@@ -216,4 +242,4 @@ FA2_EXPORT const char *fa2_strerror(int code) {
   }
 }
 
-FA2_EXPORT int fa2_version(void) { return 2; }
+FA2_EXPORT int fa2_version(void) { return 3; }

@@ -80,6 +80,8 @@ struct Params {
   void *o;
   float *lse;
   int n;          // sequence length
+  int h;          // query heads per batch index
+  int group;      // query heads per K/V head
   int n_qblocks;  // ceil(n / 128)
   int total;      // bh * n_qblocks (grid size)
   float c;        // scale * log2(e)
@@ -318,8 +320,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int head_bytes = N * D * 2;  // < 2^31 (host-validated)
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(p.q + head), 0, head_bytes, kBufWord3);
-  const uint16_t *kh = p.k + head;
-  const uint16_t *vh = p.v + head;
+  // K/V head shared by `group` consecutive query heads (grouped-query
+  // attention; 1 = one K/V head per query head)
+  const int kvbh = p.group == 1 ? bh : (bh / p.h) * (p.h / p.group) + (bh % p.h) / p.group;
+  const size_t kvhead = static_cast<size_t>(kvbh) * N * D;
+  const uint16_t *kh = p.k + kvhead;
+  const uint16_t *vh = p.v + kvhead;
 
   const int q0 = qb * kRows;      // first query of the block
   const int qw = q0 + wv * 32;    // first query of this wave
@@ -520,6 +526,8 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s) {
   prm.o = a.o;
   prm.lse = a.lse;
   prm.n = a.n;
+  prm.h = a.h;
+  prm.group = a.group;
   prm.n_qblocks = (a.n + kRows - 1) / kRows;
   prm.total = a.bh * prm.n_qblocks;
   prm.c = a.scale * kLog2e;

@@ -10,10 +10,13 @@ namespace fa2 {
 // Arguments shared by every forward kernel.  All pointers are device
 // pointers; shapes have been validated by the caller.
 struct FwdArgs {
-  const void *q, *k, *v;  // [B*H][N][d]
+  const void *q;          // [B*H][N][d]
+  const void *k, *v;      // [B*H_kv][N][d]
   void *o;                // [B*H][N][d]
   float *lse;             // [B*H][N] or nullptr
   int bh;                 // B*H
+  int h;                  // H, query heads per batch index
+  int group;              // H / H_kv, query heads per K/V head (1: none shared)
   int n;                  // sequence length
   int d;                  // head dimension (64 or 128)
   float scale;            // multiplies q.k

@@ -8,7 +8,8 @@ between the two.
 The pages measure on no dataset; the workloads are synthetic by design:
 
 * Q, K, V are drawn as ``torch.randn`` in float32 from a CPU generator
-  seeded once per call (default seed 1234), in the order q, k, v;
+  seeded once per call (default seed 1234), in the order q, k, v (K and V
+  with H_kv heads when the workload shares K/V heads between query heads);
 * the outlier workload additionally picks, for Q and then for K, for every
   (batch, head) in order, ``floor(0.05 * N)`` distinct rows with
   ``torch.randperm`` from the same generator and multiplies those whole rows
@@ -40,6 +41,7 @@ class Workload:
     causal: bool
     dtype: str  # "bf16" or "fp32": the type Q, K, V are stored in
     outliers: bool = False  # 5 % of Q and K rows scaled by 20
+    H_kv: int = 0  # K/V heads (grouped-query attention); 0 means H
 
     @property
     def scale(self) -> float:
@@ -51,9 +53,15 @@ class Workload:
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
+
     def describe(self) -> str:
-        return "B=%d,H=%d,N=%d,d=%d,%s,%s%s" % (
-            self.B, self.H, self.N, self.d,
+        return "B=%d,H=%d%s,N=%d,d=%d,%s,%s%s" % (
+            self.B, self.H,
+            (",H_kv=%d" % self.kv_heads) if self.kv_heads != self.H else "",
+            self.N, self.d,
             "causal" if self.causal else "non-causal", self.dtype,
             ",5%-rows-x20-outliers" if self.outliers else "")
 
@@ -68,25 +76,31 @@ WORKLOADS = {
         Workload("longseq_causal_b1h16_n32768_d128", 1, 16, 32768, 128, True, "bf16"),
         Workload("outlier_b4h32_n4096_d128", 4, 32, 4096, 128, False, "bf16",
                  outliers=True),
+        # grouped-query attention: the headline shape with 8 query heads per
+        # K/V head
+        Workload("gqa_causal_b2h16kv2_n8192_d128", 2, 16, 8192, 128, True,
+                 "bf16", H_kv=2),
     ]
 }
 HEADLINE = "causal_b2h16_n8192_d128"
 
 
 def make_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16",
-                seed: int = DEFAULT_SEED, outliers: bool = False):
-    """Return CPU tensors ``(q, k, v)`` of shape ``[B, H, N, d]``."""
+                seed: int = DEFAULT_SEED, outliers: bool = False, H_kv: int = 0):
+    """Return CPU tensors ``(q, k, v)``: q ``[B, H, N, d]``, k and v
+    ``[B, H_kv, N, d]`` (``H_kv`` = 0 means H)."""
     if dtype not in ("bf16", "fp32"):
         raise ValueError("dtype must be 'bf16' or 'fp32'")
+    hk = H_kv or H
     g = torch.Generator(device="cpu").manual_seed(int(seed))
     q = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
-    k = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
-    v = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    k = torch.randn(B, hk, N, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, hk, N, d, generator=g, dtype=torch.float32)
     if outliers:
         n_out = int(math.floor(0.05 * N))
         for t in (q, k):
             for b in range(B):
-                for h in range(H):
+                for h in range(t.shape[1]):
                     rows = torch.randperm(N, generator=g)[:n_out]
                     t[b, h, rows] *= 20.0
     if dtype == "bf16":
@@ -104,4 +118,4 @@ def make_dout(B: int, H: int, N: int, d: int, seed: int = DEFAULT_SEED + 1):
 def workload_inputs(w: Workload, seed: int = DEFAULT_SEED):
     """Inputs of a named workload (CPU tensors)."""
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed=seed,
-                       outliers=w.outliers)
+                       outliers=w.outliers, H_kv=w.H_kv)

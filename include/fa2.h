@@ -58,7 +58,8 @@ extern "C" {
 
 #define FA2_OK 0
 #define FA2_ERR_NULL (-1)    /* a required pointer is NULL                     */
-#define FA2_ERR_SHAPE (-2)   /* B, H or N < 1, or a size limit below exceeded */
+#define FA2_ERR_SHAPE (-2)   /* B, H, N < 1, H_kv not dividing H, or a size
+                                limit below exceeded                          */
 #define FA2_ERR_HEADDIM (-3) /* d is not 64 or 128                             */
 #define FA2_ERR_SCALE (-4)   /* scale is NaN or infinite                       */
 #define FA2_ERR_ALIGN (-5)   /* a pointer is not 16-byte aligned               */
@@ -99,6 +100,26 @@ int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 int fa2_fwd_o32(const void *q, const void *k, const void *v, float *o,
                 float *lse, int B, int H, int N, int d, float scale,
                 int causal, void *stream);
+
+/*
+ * fa2_fwd_gqa -- as fa2_fwd with H_kv <= H key/value heads shared by the
+ * query heads (grouped-query attention; H_kv == 1 is multi-query
+ * attention; H_kv == H is fa2_fwd).  FlashAttention-2 lists support for both
+ * variants among its improvements (unite.ai page "Flash Attention:
+ * revolutionising transformer efficiency", section "FlashAttention-2").
+ *   q, o : bf16 [B][H][N][d];  k, v : const bf16 [B][H_kv][N][d]
+ *   H_kv : >= 1 and dividing H (else FA2_ERR_SHAPE); query head h of batch
+ *          index b uses key/value head h / (H / H_kv) of the same b
+ * Every other argument, the lse output and the error rules are fa2_fwd's.
+ */
+int fa2_fwd_gqa(const void *q, const void *k, const void *v, void *o,
+                float *lse, int B, int H, int H_kv, int N, int d, float scale,
+                int causal, void *stream);
+
+/* fa2_fwd_gqa_o32 -- fa2_fwd_gqa with a float [B][H][N][d] output. */
+int fa2_fwd_gqa_o32(const void *q, const void *k, const void *v, float *o,
+                    float *lse, int B, int H, int H_kv, int N, int d,
+                    float scale, int causal, void *stream);
 
 /*
  * fa2_fwd_fp32 -- float32 q, k, v and o; every step (scores, softmax,
@@ -148,7 +169,7 @@ int fa2_bwd_o32(const void *q, const void *k, const void *v, const void *o,
 /* Static English description of a return code (never NULL). */
 const char *fa2_strerror(int code);
 
-/* Library ABI version: 2 (1 had the forward entry points only). */
+/* Library ABI version: 3 (2 added the backward pass, 3 grouped K/V heads). */
 int fa2_version(void);
 
 #ifdef __cplusplus

@@ -232,3 +232,24 @@ def probs(q, k, scale: float, causal: bool = False):
 def attention_bwd(q, k, v, dout, scale: float, causal: bool = False,
                   nthreads: int = 0):
     return _default().attention_bwd(q, k, v, dout, scale, causal, nthreads)
+
+
+def expand_kv_heads(kv, heads: int):
+    """Grouped-query attention by its definition: query head h of H uses
+    key/value head h // (H / H_kv).  ``kv``: ``[..., H_kv, N, d]``; returns
+    ``[..., H, N, d]`` float64 with each K/V head repeated for its group of
+    consecutive query heads."""
+    kv = _f64(kv)
+    hk = kv.shape[-3]
+    if heads % hk != 0:
+        raise ValueError("H_kv = %d does not divide H = %d" % (hk, heads))
+    return np.repeat(kv, heads // hk, axis=-3)
+
+
+def attention_gqa(q, k, v, scale: float, causal: bool = False, nthreads: int = 0):
+    """Exact attention with grouped K/V heads: ``q`` ``[..., H, N, d]``,
+    ``k``, ``v`` ``[..., H_kv, N, d]`` (H_kv dividing H).  Returns
+    ``(o, lse, threads_used)`` as :func:`attention`."""
+    h = _f64(q).shape[-3]
+    return attention(q, expand_kv_heads(k, h), expand_kv_heads(v, h), scale,
+                     causal, nthreads)

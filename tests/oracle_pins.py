@@ -292,6 +292,28 @@ def pin_rows_match_full(orc):
         _close(lrow, lse[0, rows], tol=0, what="rows lse")
 
 
+def pin_gqa_head_map(orc):
+    """Grouped K/V heads: with every value row of K/V head g equal to the
+    constant g + 1, the output of query head h is exactly h // (H / H_kv) + 1
+    (a constant V passes through the softmax), which fixes the head map; with
+    H_kv = H the grouped call is the plain one."""
+    import oracle as orc_mod
+    r = _rng(30)
+    B, H, Hk, N, d = 2, 6, 2, 9, 4
+    q = r.standard_normal((B, H, N, d))
+    k = r.standard_normal((B, Hk, N, d))
+    v = np.empty((B, Hk, N, d))
+    for g in range(Hk):
+        v[:, g] = g + 1.0
+    kx = orc_mod.expand_kv_heads(k, H)
+    vx = orc_mod.expand_kv_heads(v, H)
+    o, _, _ = orc.attention(q, kx, vx, 0.5, True)
+    for h in range(H):
+        _close(o[:, h], np.full((B, N, d), h // (H // Hk) + 1.0), what="gqa head %d" % h)
+    k2 = r.standard_normal((B, H, N, d))
+    assert np.array_equal(orc_mod.expand_kv_heads(k2, H), k2)
+
+
 # ---------------------------------------------------------------------------
 # gradients
 
@@ -441,6 +463,7 @@ ALL_PINS = [
     pin_online_merge,
     pin_brute_force,
     pin_rows_match_full,
+    pin_gqa_head_map,
     pin_bwd_finite_differences,
     pin_bwd_sums,
     pin_bwd_constant_v,

@@ -50,7 +50,7 @@ def test_codes_match_header():
 
 
 def test_version_and_strerror(L):
-    assert fa2.version() == 2
+    assert fa2.version() == 3
     seen = set()
     for name, code in header_codes().items():
         msg = fa2.strerror(code)
@@ -184,3 +184,29 @@ def test_bwd_binding_checks():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         fa2.backward(q, q, q, q, q, torch.zeros(1, 1, 8))
+
+
+# Grouped-query forward: H_kv K/V heads
+GQA_FUNCS = ("fa2_fwd_gqa", "fa2_fwd_gqa_o32")
+
+
+def call_gqa(fn, H=4, H_kv=2, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa2.raw_call(fn, a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                        H, a["N"], a["d"], a["scale"], a["causal"], H_kv=H_kv)
+
+
+@pytest.mark.parametrize("fn", GQA_FUNCS)
+def test_gqa_validation(L, fn):
+    for H, H_kv in ((4, 0), (4, -1), (4, 3), (2, 4), (6, 4)):
+        assert call_gqa(fn, H, H_kv) == fa2.FA2_ERR_SHAPE, (H, H_kv)
+    for key in ("q", "k", "v", "o"):
+        assert call_gqa(fn, **{key: None}) == fa2.FA2_ERR_NULL, key
+    assert call_gqa(fn, d=96) == fa2.FA2_ERR_HEADDIM
+    assert call_gqa(fn, scale=float("nan")) == fa2.FA2_ERR_SCALE
+    assert call_gqa(fn, v=GOOD["v"] + 8) == fa2.FA2_ERR_ALIGN
+    # K and V spans are B*H_kv*N*d elements: o right after the end of k
+    # (1*2*64*64 bf16 = 16 KiB) is fine only if it does not overlap
+    assert call_gqa(fn, o=GOOD["k"] + 16 * 1024 - 16) == fa2.FA2_ERR_ALIAS
+    assert call_gqa(fn, lse=GOOD["v"] + 4096) == fa2.FA2_ERR_ALIAS

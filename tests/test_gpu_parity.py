@@ -140,7 +140,11 @@ def test_full_size_workload(fa2, name):
     rng = np.random.default_rng(5)
     heads = sorted({0, BH // 2, BH - 1})
     rows = sample_rows(w.N, rng)
-    qf, kf, vf = (t.reshape(BH, w.N, w.d) for t in (q, k, v))
+    kx, vx = k, v
+    if w.kv_heads != w.H:  # grouped K/V heads, by their definition
+        kx = oracle.expand_kv_heads(k, w.H)
+        vx = oracle.expand_kv_heads(v, w.H)
+    qf, kf, vf = (t.reshape(BH, w.N, w.d) for t in (q, kx, vx))
     refs = {}
     for h in heads:
         refs[h] = oracle.attention_rows(qf[h, rows], rows, kf[h], vf[h],

@@ -44,6 +44,21 @@ def test_bwd_threads_repeatable(orc):
     assert a[4] == 3 and c[4] == 1
 
 
+def test_gqa_pin_rejects_an_interleaved_head_map(orc, monkeypatch):
+    """A plausible mistake in the grouped-head map -- query head h using K/V
+    head h % H_kv instead of h // (H / H_kv) -- fails the head-map pin."""
+    import oracle as orc_mod
+    from oracle_pins import pin_gqa_head_map
+
+    def interleaved(kv, heads):
+        kv = np.asarray(kv, dtype=np.float64)
+        return np.tile(kv, (1,) * (kv.ndim - 3) + (heads // kv.shape[-3], 1, 1))
+
+    monkeypatch.setattr(orc_mod, "expand_kv_heads", interleaved)
+    with pytest.raises(AssertionError):
+        pin_gqa_head_map(orc)
+
+
 def test_merge_reading_o2_unnormalised(orc):
     """The online-softmax section's O update weights the new block by
     e^(m2-m)/l without an l2 factor; that is only consistent if the new
