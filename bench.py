@@ -9,7 +9,9 @@ headline workload B=2, H=16, N=8192, d=128, causal, inputs resident in HBM
 ``--seq-len`` pick another shape).  ``--pass bwd`` times ``fa2_bwd`` instead
 (gradients for a seeded dO, after one forward call that provides O and lse),
 counted at the usual 2.5x the forward's flop: the five products S, dP, dV,
-dK, dQ.
+dK, dQ.  Workloads with fewer query rows than keys (decoding) run through
+``fa2_fwd_splitkv`` with its default key-range split and are reported
+against the HBM roofline (their bytes: K, V, Q read, O and lse written).
 W untimed warm-up steps are followed by exactly K timed steps between HIP
 events on the stream the kernel is launched on.  Rank 0 prints one JSON line:
 TFLOP/s (4*B*H*N^2*d, halved for causal), the roofline of the kernel against
@@ -40,6 +42,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "exact_io_aware_24_amd", "csrc")
 KERNEL_SRCS = {"fwd": ("fa2_fwd_bf16.hip", "fa2_device.h"),
                "bwd": ("fa2_bwd_bf16.hip", "fa2_device.h")}
@@ -52,10 +55,14 @@ def score_matrix_bytes(B: int, H: int, N: int, elem_bytes: int = 2) -> float:
     return float(B) * H * N * N * elem_bytes
 
 
-def compulsory_bytes(B, H, N, d, in_bytes=2, out_bytes=2, lse=True) -> float:
+def compulsory_bytes(B, H, N, d, in_bytes=2, out_bytes=2, lse=True,
+                     Nq=None, H_kv=None) -> float:
     """Q, K, V read once, O (and lse) written once."""
-    n = float(B) * H * N * d
-    return 3 * n * in_bytes + n * out_bytes + (float(B) * H * N * 4 if lse else 0)
+    Nq = N if Nq is None else Nq
+    H_kv = H if H_kv is None else H_kv
+    nq = float(B) * H * Nq * d
+    nkv = float(B) * H_kv * N * d
+    return (nq + 2 * nkv) * in_bytes + nq * out_bytes + (float(B) * H * Nq * 4 if lse else 0)
 
 
 def kernel_source_hash(which: str = "fwd") -> str:
@@ -129,25 +136,28 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     if w.kv_heads != w.H:  # grouped K/V heads: the oracle's definition
         k = torch.from_numpy(oracle.expand_kv_heads(k, w.H))
         v = torch.from_numpy(oracle.expand_kv_heads(v, w.H))
-    qf, kf, vf = (t.reshape(BH, w.N, w.d) for t in (q, k, v))
+    nq = w.q_rows
+    qf = q.reshape(BH, nq, w.d)
+    kf, vf = (t.reshape(BH, w.N, w.d) for t in (k, v))
+    off = w.N - nq  # causal: query i at key position i + off
 
     def head_flops(rows):
-        keys = (rows + 1) if w.causal else np.full(rows.shape, w.N)
+        keys = np.clip(rows + off + 1, 0, w.N) if w.causal else np.full(rows.shape, w.N)
         return float(np.sum(4.0 * w.d * keys))
 
     # calibration: every 16th row of head 0
-    rows = np.arange(0, w.N, 16, dtype=np.int64)
+    rows = np.arange(0, nq, 16, dtype=np.int64)
     t0 = time.perf_counter()
-    _, _, threads = oracle.attention_rows(qf[0, rows], rows, kf[0], vf[0],
+    _, _, threads = oracle.attention_rows(qf[0, rows], rows + off, kf[0], vf[0],
                                           w.scale, w.causal)
     rate = head_flops(rows) / max(time.perf_counter() - t0, 1e-9)
-    all_rows = np.arange(w.N, dtype=np.int64)
+    all_rows = np.arange(nq, dtype=np.int64)
     per_head = head_flops(all_rows)
     n_heads = int(max(1, min(BH, round(budget_s * rate / per_head))))
     t0 = time.perf_counter()
     for h in range(n_heads):
-        _, _, threads = oracle.attention(qf[h:h + 1], kf[h:h + 1], vf[h:h + 1],
-                                         w.scale, w.causal)
+        _, _, threads = oracle.attention_offset(qf[h:h + 1], kf[h:h + 1], vf[h:h + 1],
+                                                w.scale, w.causal)
     dt = time.perf_counter() - t0
     flops = per_head * n_heads
     return {
@@ -157,7 +167,7 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         "kind": "oracle",
         "sample": "%d of %d heads (all %d query rows each) of %s; fp64 C oracle, "
                   "%.1f s wall, %.3g flop counted like the GPU metric"
-                  % (n_heads, BH, w.N, w.describe(), dt, flops),
+                  % (n_heads, BH, nq, w.describe(), dt, flops),
     }
 
 
@@ -222,12 +232,31 @@ def main(argv=None):
     if args.which == "bwd" and w.kv_heads != w.H:
         print("the backward pass takes one K/V head per query head", file=sys.stderr)
         return 2
+    decode = w.q_rows != w.N
+    if decode and (args.which == "bwd" or entry != "fa2_fwd" or args.seq_len):
+        print("workloads with fewer queries than keys time fa2_fwd_splitkv only",
+              file=sys.stderr)
+        return 2
     q, k, v = wl.make_inputs(w.B, w.H, w.N, w.d, w.dtype, outliers=w.outliers,
-                             H_kv=w.H_kv)
+                             H_kv=w.H_kv, Nq=w.Nq)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     out_dtype = torch.float32 if entry.endswith("_o32") else torch.bfloat16
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
-    if args.which == "fwd":
+    n_splits = None
+    if decode:
+        flops = w.flops
+        entry = "fa2_fwd_splitkv"
+        n_splits = fa2.default_splits(w.B, w.H, w.q_rows, w.N, w.d)
+        o = torch.empty(qd.shape, dtype=out_dtype, device=dev)
+        o_part = torch.empty((n_splits,) + tuple(qd.shape), dtype=torch.float32, device=dev)
+        lse_part = torch.empty((n_splits,) + tuple(qd.shape[:3]), dtype=torch.float32,
+                               device=dev)
+
+        def step():
+            fa2.forward_splitkv(qd, kd, vd, causal=w.causal, scale=w.scale,
+                                n_splits=n_splits, out=o, lse=lse, o_part=o_part,
+                                lse_part=lse_part)
+    elif args.which == "fwd":
         flops = w.flops
         o = torch.empty(qd.shape, dtype=out_dtype, device=dev)
 
@@ -289,6 +318,16 @@ def main(argv=None):
 
     same_shape = not args.seq_len and entry == "fa2_" + args.which
     traffic = read_traffic(name, args.which) if same_shape else None
+    comp = compulsory_bytes(w.B, w.H, w.N, w.d, Nq=w.q_rows, H_kv=w.kv_heads)
+    if decode:  # bandwidth-bound: K and V are read once, little arithmetic
+        gbs = comp / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
     rec = {
         "metric": "attention %s TFLOP/s (1 MI355X) and %% of bf16 MFMA peak" % args.which,
         "value": round(tflops, 3),
@@ -302,20 +341,14 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded randn, bf16)",
-        "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "scale": w.scale,
-                   "flops_per_step": flops, "entry_point": entry},
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(tflops, 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-        },
+        "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads,
+                   "Nq": w.q_rows, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": w.scale, "flops_per_step": flops, "entry_point": entry,
+                   "n_splits": n_splits},
+        "roofline": roofline,
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "score_matrix_bytes_not_written": score_matrix_bytes(w.B, w.H, w.N),
-        "compulsory_hbm_bytes": compulsory_bytes(w.B, w.H, w.N, w.d),
+        "compulsory_hbm_bytes": comp,
         "kernel_source_sha256": kernel_source_hash(args.which),
         "gpu": torch.cuda.get_device_name(dev),
     }

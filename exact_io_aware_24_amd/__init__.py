@@ -31,8 +31,9 @@ FA2_ERR_HIP = -7
 
 # Every symbol include/fa2.h declares.
 EXPORTED = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_gqa", "fa2_fwd_gqa_o32",
-            "fa2_fwd_fp32", "fa2_bwd", "fa2_bwd_o32", "fa2_strerror",
-            "fa2_version")
+            "fa2_fwd_splitkv", "fa2_fwd_splitkv_o32", "fa2_fwd_fp32", "fa2_bwd",
+            "fa2_bwd_o32", "fa2_strerror", "fa2_version")
+MAX_SPLITS = 1024  # FA2_MAX_SPLITS
 
 _lock = threading.Lock()
 _lib = None
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
         for name in ("fa2_fwd_gqa", "fa2_fwd_gqa_o32"):
             f = getattr(L, name)
             f.argtypes = gsig
+            f.restype = ctypes.c_int
+        ssig = [vp] * 5 + [i] * 6 + [ctypes.c_float, i, i, vp, vp, vp]
+        for name in ("fa2_fwd_splitkv", "fa2_fwd_splitkv_o32"):
+            f = getattr(L, name)
+            f.argtypes = ssig
             f.restype = ctypes.c_int
         bsig = [vp] * 10 + [i, i, i, i, ctypes.c_float, i, vp]
         for name in ("fa2_bwd", "fa2_bwd_o32"):
@@ -252,6 +258,79 @@ def backward(q, k, v, o, dout, lse, causal: bool = False,
     if rc != FA2_OK:
         raise FA2Error(rc, fn)
     return dq, dk, dv
+
+
+def default_splits(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    """A key-range count that gives the GPU about 1024 workgroups (two per
+    compute unit, twice over) while keeping every range at least four key
+    tiles long."""
+    blocks = B * H * ((Nq + 127) // 128)
+    tile = 64 if d == 128 else 128
+    tiles = (Nk + tile - 1) // tile
+    n = -(-1024 // blocks)
+    return int(max(1, min(n, tiles // 4, MAX_SPLITS)))
+
+
+def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
+                    n_splits: int | None = None, out_dtype=None, out=None,
+                    lse=None, o_part=None, lse_part=None, return_lse: bool = True):
+    """General forward (``fa2_fwd_splitkv[_o32]``): ``q`` ``[B, H, Nq, d]``
+    against ``k, v`` ``[B, H_kv, Nk, d]`` (bfloat16, H_kv dividing H), the
+    keys of each query block split into ``n_splits`` ranges that are merged
+    afterwards (default: :func:`default_splits`).  Causal: query i sits at
+    key position ``i + Nk - Nq``.  Workspaces ``o_part`` (float32
+    ``[n_splits, B, H, Nq, d]``) and ``lse_part`` (``[n_splits, B, H, Nq]``)
+    are allocated when not given.  Returns ``(o, lse)``."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_cuda \
+                or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be a contiguous bfloat16 GPU tensor [B, H, N, d]" % name)
+    B, H, Nq, d = (int(x) for x in q.shape)
+    H_kv, Nk = int(k.shape[1]), int(k.shape[2])
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d or H_kv < 1 \
+            or H % H_kv != 0 or not (q.device == k.device == v.device):
+        raise ValueError("k, v must be [B, H_kv, Nk, d] with H_kv dividing H")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_splits is None:
+        n_splits = default_splits(B, H, Nq, Nk, d)
+    odt = torch.bfloat16 if out_dtype is None else out_dtype
+    fn = {torch.bfloat16: "fa2_fwd_splitkv", torch.float32: "fa2_fwd_splitkv_o32"}.get(odt)
+    if fn is None:
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=odt, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    if n_splits > 1:
+        if o_part is None:
+            o_part = torch.empty((n_splits, B, H, Nq, d), dtype=torch.float32, device=dev)
+        if lse_part is None:
+            lse_part = torch.empty((n_splits, B, H, Nq), dtype=torch.float32, device=dev)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = getattr(lib(), fn)(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ptr(lse),
+            B, H, H_kv, Nq, Nk, d, ctypes.c_float(scale), int(bool(causal)),
+            int(n_splits), ptr(o_part), ptr(lse_part), stream)
+    if rc != FA2_OK:
+        raise FA2Error(rc, fn)
+    return out, lse
+
+
+def raw_call_splitkv(fn: str, ptrs, B, H, H_kv, Nq, Nk, d, scale, causal,
+                     n_splits, stream=None) -> int:
+    """Call a split-KV entry point with raw pointers (q, k, v, o, lse,
+    o_part, lse_part); returns the code."""
+    q, k, v, o, lse, op, lp = ptrs
+    return int(getattr(lib(), fn)(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d,
+                                  ctypes.c_float(scale), int(causal), n_splits,
+                                  op, lp, stream))
 
 
 def raw_call_bwd(fn: str, ptrs, B, H, N, d, scale, causal, stream=None) -> int:

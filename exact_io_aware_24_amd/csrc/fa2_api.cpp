@@ -33,31 +33,34 @@ bool misaligned(const void *p) {
 // addresses one head with 32-bit byte offsets, including one tile of reads
 // past the end that the hardware bounds check turns into zeros).
 int validate(const void *q, const void *k, const void *v, const void *o,
-             const float *lse, int B, int H, int H_kv, int N, int d,
+             const float *lse, int B, int H, int H_kv, int Nq, int Nk, int d,
              float scale, int in_bytes, int out_bytes, int rows_per_block,
              int64_t max_per_head) {
   if (!q || !k || !v || !o) return FA2_ERR_NULL;
-  if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H % H_kv != 0) return FA2_ERR_SHAPE;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || H_kv < 1 || H % H_kv != 0)
+    return FA2_ERR_SHAPE;
   if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
   const int64_t bh = static_cast<int64_t>(B) * H;
-  const int64_t per_head = static_cast<int64_t>(N) * d;
-  const int64_t blocks = bh * ((static_cast<int64_t>(N) + rows_per_block - 1) /
+  const int64_t q_head = static_cast<int64_t>(Nq) * d;
+  const int64_t kv_head = static_cast<int64_t>(Nk) * d;
+  const int64_t blocks = bh * ((static_cast<int64_t>(Nq) + rows_per_block - 1) /
                                rows_per_block);
-  if (bh > INT32_MAX || per_head > max_per_head || blocks > INT32_MAX ||
-      bh * per_head > FA2_MAX_ELEMS)
+  if (bh > INT32_MAX || q_head > max_per_head || kv_head > max_per_head ||
+      blocks > INT32_MAX || bh * q_head > FA2_MAX_ELEMS ||
+      bh * kv_head > FA2_MAX_ELEMS)
     return FA2_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA2_ERR_SCALE;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
       (lse && misaligned(lse)))
     return FA2_ERR_ALIGN;
-  const int64_t elems = bh * per_head;
-  const int64_t kv_elems = static_cast<int64_t>(B) * H_kv * per_head;
+  const int64_t elems = bh * q_head;
+  const int64_t kv_elems = static_cast<int64_t>(B) * H_kv * kv_head;
   const Range rq = span(q, elems * in_bytes), rk = span(k, kv_elems * in_bytes),
               rv = span(v, kv_elems * in_bytes), ro = span(o, elems * out_bytes);
   if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv))
     return FA2_ERR_ALIAS;
   if (lse) {
-    const Range rl = span(lse, bh * N * static_cast<int64_t>(sizeof(float)));
+    const Range rl = span(lse, bh * Nq * static_cast<int64_t>(sizeof(float)));
     if (overlaps(rl, rq) || overlaps(rl, rk) || overlaps(rl, rv) ||
         overlaps(rl, ro))
       return FA2_ERR_ALIAS;
@@ -66,8 +69,8 @@ int validate(const void *q, const void *k, const void *v, const void *o,
 }
 
 fa2::FwdArgs make_args(const void *q, const void *k, const void *v, void *o,
-                       float *lse, int B, int H, int H_kv, int N, int d,
-                       float scale, int causal) {
+                       float *lse, int B, int H, int H_kv, int Nq, int Nk,
+                       int d, float scale, int causal) {
   fa2::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -77,7 +80,11 @@ fa2::FwdArgs make_args(const void *q, const void *k, const void *v, void *o,
   a.bh = B * H;
   a.h = H;
   a.group = H / H_kv;
-  a.n = N;
+  a.nq = Nq;
+  a.nk = Nk;
+  a.n_splits = 1;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
   a.d = d;
   a.scale = scale;
   a.causal = causal != 0;
@@ -94,7 +101,7 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o,
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv)
     return FA2_ERR_NULL;
   // shape, head dimension, size limits and scale as for the forward
-  int rc = validate(q, k, v, o, nullptr, B, H, H, N, d, scale, 2, 2,
+  int rc = validate(q, k, v, o, nullptr, B, H, H, N, N, d, scale, 2, 2,
                     fa2::kBf16BwdRowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK && rc != FA2_ERR_ALIAS) return rc;
   if (misaligned(dout) || misaligned(lse) || misaligned(delta) ||
@@ -146,22 +153,22 @@ int finish(hipError_t e) { return e == hipSuccess ? FA2_OK : FA2_ERR_HIP; }
 FA2_EXPORT int fa2_fwd(const void *q, const void *k, const void *v, void *o,
                        float *lse, int B, int H, int N, int d, float scale,
                        int causal, void *stream) {
-  int rc = validate(q, k, v, o, lse, B, H, H, N, d, scale, 2, 2,
+  int rc = validate(q, k, v, o, lse, B, H, H, N, N, d, scale, 2, 2,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
-      make_args(q, k, v, o, lse, B, H, H, N, d, scale, causal), false,
+      make_args(q, k, v, o, lse, B, H, H, N, N, d, scale, causal), false,
       static_cast<hipStream_t>(stream)));
 }
 
 FA2_EXPORT int fa2_fwd_gqa(const void *q, const void *k, const void *v,
                            void *o, float *lse, int B, int H, int H_kv, int N,
                            int d, float scale, int causal, void *stream) {
-  int rc = validate(q, k, v, o, lse, B, H, H_kv, N, d, scale, 2, 2,
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, 2, 2,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
-      make_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal), false,
+      make_args(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, causal), false,
       static_cast<hipStream_t>(stream)));
 }
 
@@ -169,33 +176,88 @@ FA2_EXPORT int fa2_fwd_gqa_o32(const void *q, const void *k, const void *v,
                                float *o, float *lse, int B, int H, int H_kv,
                                int N, int d, float scale, int causal,
                                void *stream) {
-  int rc = validate(q, k, v, o, lse, B, H, H_kv, N, d, scale, 2, 4,
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, 2, 4,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
-      make_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal), true,
+      make_args(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, causal), true,
       static_cast<hipStream_t>(stream)));
 }
 
 FA2_EXPORT int fa2_fwd_o32(const void *q, const void *k, const void *v,
                            float *o, float *lse, int B, int H, int N, int d,
                            float scale, int causal, void *stream) {
-  int rc = validate(q, k, v, o, lse, B, H, H, N, d, scale, 2, 4,
+  int rc = validate(q, k, v, o, lse, B, H, H, N, N, d, scale, 2, 4,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
-      make_args(q, k, v, o, lse, B, H, H, N, d, scale, causal), true,
+      make_args(q, k, v, o, lse, B, H, H, N, N, d, scale, causal), true,
       static_cast<hipStream_t>(stream)));
+}
+
+// Key ranges of one query block computed by separate workgroups, then
+// merged: the same kernel with a key range per workgroup writing fp32
+// partial (O, lse), and a merge kernel.  n_splits == 1 is a plain call.
+static int splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+            int B, int H, int H_kv, int Nq, int Nk, int d, float scale,
+            int causal, int n_splits, float *o_part, float *lse_part,
+            bool o32, void *stream) {
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, 2,
+                    o32 ? 4 : 2, fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc != FA2_OK) return rc;
+  if (n_splits < 1 || n_splits > FA2_MAX_SPLITS) return FA2_ERR_SHAPE;
+  const int64_t bh = static_cast<int64_t>(B) * H;
+  const int64_t blocks = bh * ((static_cast<int64_t>(Nq) + fa2::kBf16RowsPerBlock - 1) /
+                               fa2::kBf16RowsPerBlock);
+  if (blocks * n_splits > INT32_MAX) return FA2_ERR_SHAPE;
+  if (n_splits > 1) {
+    if (!o_part || !lse_part) return FA2_ERR_NULL;
+    if (misaligned(o_part) || misaligned(lse_part)) return FA2_ERR_ALIGN;
+    const int64_t rows = bh * Nq;
+    const int64_t kv = static_cast<int64_t>(B) * H_kv * Nk * d * 2;
+    const Range parts[2] = {span(o_part, n_splits * rows * d * 4),
+                            span(lse_part, n_splits * rows * 4)};
+    const Range others[5] = {span(q, rows * d * 2), span(k, kv), span(v, kv),
+                             span(o, rows * d * (o32 ? 4 : 2)),
+                             span(lse ? lse : o_part, lse ? rows * 4 : 0)};
+    if (overlaps(parts[0], parts[1])) return FA2_ERR_ALIAS;
+    for (const Range &p : parts)
+      for (const Range &x : others)
+        if (overlaps(p, x)) return FA2_ERR_ALIAS;
+  }
+  fa2::FwdArgs a = make_args(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal);
+  a.n_splits = n_splits;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  return finish(fa2::launch_fwd_bf16(a, o32, static_cast<hipStream_t>(stream)));
+}
+
+FA2_EXPORT int fa2_fwd_splitkv(const void *q, const void *k, const void *v,
+                               void *o, float *lse, int B, int H, int H_kv,
+                               int Nq, int Nk, int d, float scale, int causal,
+                               int n_splits, float *o_part, float *lse_part,
+                               void *stream) {
+  return splitkv(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal,
+                 n_splits, o_part, lse_part, false, stream);
+}
+
+FA2_EXPORT int fa2_fwd_splitkv_o32(const void *q, const void *k, const void *v,
+                                   float *o, float *lse, int B, int H, int H_kv,
+                                   int Nq, int Nk, int d, float scale,
+                                   int causal, int n_splits, float *o_part,
+                                   float *lse_part, void *stream) {
+  return splitkv(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal,
+                 n_splits, o_part, lse_part, true, stream);
 }
 
 FA2_EXPORT int fa2_fwd_fp32(const float *q, const float *k, const float *v,
                             float *o, float *lse, int B, int H, int N, int d,
                             float scale, int causal, void *stream) {
-  int rc = validate(q, k, v, o, lse, B, H, H, N, d, scale, 4, 4,
+  int rc = validate(q, k, v, o, lse, B, H, H, N, N, d, scale, 4, 4,
                     fa2::kFp32RowsPerBlock, INT32_MAX);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_fp32(
-      make_args(q, k, v, o, lse, B, H, H, N, d, scale, causal),
+      make_args(q, k, v, o, lse, B, H, H, N, N, d, scale, causal),
       static_cast<hipStream_t>(stream)));
 }
 
@@ -242,4 +304,4 @@ FA2_EXPORT const char *fa2_strerror(int code) {
   }
 }
 
-FA2_EXPORT int fa2_version(void) { return 3; }
+FA2_EXPORT int fa2_version(void) { return 4; }

@@ -77,14 +77,19 @@ constexpr float kRescaleThreshold = 8.0f;  // base-2 units: P~ <= 256
 
 struct Params {
   const uint16_t *q, *k, *v;
-  void *o;
-  float *lse;
-  int n;          // sequence length
-  int h;          // query heads per batch index
-  int group;      // query heads per K/V head
-  int n_qblocks;  // ceil(n / 128)
-  int total;      // bh * n_qblocks (grid size)
-  float c;        // scale * log2(e)
+  void *o;               // final output, or fp32 partial outputs per split
+  float *lse;            // final lse, or partial lse per split (may be null)
+  int nq;                // query rows per head
+  int nk;                // key rows per head
+  int h;                 // query heads per batch index
+  int group;             // query heads per K/V head
+  int n_qblocks;         // ceil(nq / 128)
+  int n_splits;          // key ranges per query block (1: no split)
+  int tiles_per_split;   // key tiles per range
+  int total;             // bh * n_qblocks * n_splits (grid size)
+  size_t o_split_stride;    // elements between the partial outputs of splits
+  size_t lse_split_stride;  // same for lse
+  float c;               // scale * log2(e)
 };
 
 template <int D>
@@ -309,27 +314,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int lr = lane & 31;  // query column of this lane in S^T / O^T
   const int hh = lane >> 5;  // half-wave
 
-  // ---- workgroup -> (head, query block) ----------------------------------
-  const int logical = xcd_remap(blockIdx.x, p.total);
+  // ---- workgroup -> (head, query block, key range) -------------------------
+  int logical = xcd_remap(blockIdx.x, p.total);
+  int split = 0;
+  if (p.n_splits > 1) {
+    split = logical % p.n_splits;
+    logical /= p.n_splits;
+  }
   const int bh = logical / p.n_qblocks;
   const int qbl = logical - bh * p.n_qblocks;
   const int qb = CAUSAL ? (p.n_qblocks - 1 - qbl) : qbl;
 
-  const int N = p.n;
-  const size_t head = static_cast<size_t>(bh) * N * D;
-  const int head_bytes = N * D * 2;  // < 2^31 (host-validated)
+  const int Nq = p.nq, Nk = p.nk;
+  // causal: query i sits at key position i + Nk - Nq (the last query sees
+  // every key; with Nq == Nk, query i sees keys 0..i)
+  const int qoff = Nk - Nq;
+  const size_t qhead = static_cast<size_t>(bh) * Nq * D;
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(p.q + head), 0, head_bytes, kBufWord3);
+      const_cast<uint16_t *>(p.q + qhead), 0, Nq * D * 2, kBufWord3);
   // K/V head shared by `group` consecutive query heads (grouped-query
   // attention; 1 = one K/V head per query head)
   const int kvbh = p.group == 1 ? bh : (bh / p.h) * (p.h / p.group) + (bh % p.h) / p.group;
-  const size_t kvhead = static_cast<size_t>(kvbh) * N * D;
+  const size_t kvhead = static_cast<size_t>(kvbh) * Nk * D;
+  const int head_bytes = Nk * D * 2;  // < 2^31 (host-validated)
   const uint16_t *kh = p.k + kvhead;
   const uint16_t *vh = p.v + kvhead;
 
   const int q0 = qb * kRows;      // first query of the block
   const int qw = q0 + wv * 32;    // first query of this wave
   const int qi = qw + lr;         // this lane's query
+  const int qpos = qi + qoff;     // its position among the keys
 
   // ---- fixed offsets -------------------------------------------------------
   Offsets<D> off;
@@ -382,48 +396,56 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // Software pipeline: iteration t computes the scores of tile t+1 (K one tile
   // ahead in LDS) while it runs the softmax of tile t and the P.V product
   // with V(t); the loads of K(t+2) and V(t+1) are in flight meanwhile.
-  // Tiles [0, n_full) need no mask for any row of the block; the rest (the
-  // diagonal band when causal, the ragged end of the sequence) are masked.
-  const int kend = CAUSAL ? min(N, q0 + kRows) : N;
-  const int ntiles = (kend + C::BC - 1) / C::BC;
-  int n_full = CAUSAL ? (q0 + 1) / C::BC : N / C::BC;
-  if (n_full > ntiles) n_full = ntiles;
+  // Tiles are numbered over the whole key range; this workgroup takes tiles
+  // [tb, ntiles) of it (all of them unless the keys are split).  Tiles below
+  // n_full need no mask for any row of the block; the rest (the diagonal
+  // band when causal, the ragged end of the keys) are masked.
+  const int kend = CAUSAL ? max(0, min(Nk, q0 + kRows + qoff)) : Nk;
+  const int tb = split * p.tiles_per_split;
+  const int ntiles = min((kend + C::BC - 1) / C::BC, tb + p.tiles_per_split);
+  const int n_full = CAUSAL ? max(0, (q0 + qoff + 1) / C::BC) : Nk / C::BC;
+  // waves with no query rows (short query blocks) only help with the loads
+  const bool live = qw < Nq;
   // tiles this wave needs (causal: keys up to its last query)
-  const int w_tiles = CAUSAL ? min(ntiles, (qw + 31) / C::BC + 1) : ntiles;
+  const int w_tiles = !live ? tb
+                      : CAUSAL ? min(ntiles, (qw + 31 + qoff) / C::BC + 1) : ntiles;
   // branch-free main loop: tiles t and t+1 unmasked
-  const int n_main = min(n_full - 1, ntiles - 1);
+  const int n_main = live ? min(n_full, ntiles) - 1 : tb;
 
   auto kbuf = [&](int i) { return smem + i * C::TILE_BYTES; };
   auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE_BYTES; };
+  f32x16 sa[C::NKT], sb[C::NKT];
 
   // Rows past the end of the sequence load as zeros; clear LDS first so that
   // no tile can ever expose uninitialised bits, whatever the hardware does
   // with out-of-range lanes.
-  if (N % C::BC != 0) {
+  if (tb < ntiles) {  // (an empty key range leaves l = 0: O = 0, lse = -inf)
+  if (Nk % C::BC != 0) {
     for (int i = tid; i < 4 * C::TILE_BYTES / 16; i += kThreads)
       reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
   }
-  // prologue: K(0), V(0) -> buffers 0; then K(1) in flight while S(0) is
-  // computed.
-  issue_k<D>(kh, head_bytes, off, kbuf(0), wv, 0);
-  issue_v<D>(vh, head_bytes, off, vbuf(0), wv, 0);
+  // prologue: K(tb), V(tb) -> buffers 0; then K(tb+1) in flight while S(tb)
+  // is computed.  Buffer parity is (t - tb) & 1.
+  issue_k<D>(kh, head_bytes, off, kbuf(0), wv, tb * C::BC * D * 2);
+  issue_v<D>(vh, head_bytes, off, vbuf(0), wv, tb * C::BC * D * 2);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (ntiles > 1) issue_k<D>(kh, head_bytes, off, kbuf(1), wv, C::BC * D * 2);
-  f32x16 sa[C::NKT], sb[C::NKT];
-  scores<D>(kbuf(0), off, st.qreg, sa);
-  if (n_full > 0)
-    softmax_max<D, CAUSAL, false>(sa, st, c, 0, N, qi, hh);
-  else
-    softmax_max<D, CAUSAL, true>(sa, st, c, 0, N, qi, hh);
+  if (tb + 1 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(1), wv, (tb + 1) * C::BC * D * 2);
+  if (tb < w_tiles) {
+    scores<D>(kbuf(0), off, st.qreg, sa);
+    if (tb < n_full)
+      softmax_max<D, CAUSAL, false>(sa, st, c, tb * C::BC, Nk, qpos, hh);
+    else
+      softmax_max<D, CAUSAL, true>(sa, st, c, tb * C::BC, Nk, qpos, hh);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // one pipelined iteration; CUR holds S(t), NXT receives S(t+1)
   auto step = [&](auto par_tag, int t, f32x16(&cur)[C::NKT],
                   f32x16(&nxt)[C::NKT]) {
-    constexpr int P = decltype(par_tag)::value;  // t & 1
+    constexpr int P = decltype(par_tag)::value;  // (t - tb) & 1
     const int j0 = t * C::BC;
     if (t + 2 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(P), wv, (j0 + 2 * C::BC) * D * 2);
     issue_v<D>(vh, head_bytes, off, vbuf(1 - P), wv, (j0 + C::BC) * D * 2);
@@ -431,14 +453,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     bf16x8 pb[C::NKT][2];
     softmax_exp<D, false>(cur, st.m_run, c, pb, st.l_run);
     pv<D>(vbuf(P), off, pb, st.oacc);
-    softmax_max<D, CAUSAL, false>(nxt, st, c, j0 + C::BC, N, qi, hh);
+    softmax_max<D, CAUSAL, false>(nxt, st, c, j0 + C::BC, Nk, qpos, hh);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
 
-  int t = 0;
+  int t = tb;
   for (; t + 2 <= n_main; t += 2) {
     step(P0{}, t, sa, sb);
     step(P1{}, t + 1, sb, sa);
@@ -452,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // general loop: masked tiles, waves that stop early, the last tile
   for (; t < ntiles; ++t) {
     const int j0 = t * C::BC;
-    const int p = t & 1;
+    const int p = (t - tb) & 1;
     if (t + 2 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(p), wv, (j0 + 2 * C::BC) * D * 2);
     if (t + 1 < ntiles) issue_v<D>(vh, head_bytes, off, vbuf(1 - p), wv, (j0 + C::BC) * D * 2);
     if (t + 1 < w_tiles) scores<D>(kbuf(1 - p), off, st.qreg, sb);
@@ -463,19 +485,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       pv<D>(vbuf(p), off, pb, st.oacc);
     }
     if (t + 1 < w_tiles)
-      softmax_max<D, CAUSAL, true>(sb, st, c, j0 + C::BC, N, qi, hh);
+      softmax_max<D, CAUSAL, true>(sb, st, c, j0 + C::BC, Nk, qpos, hh);
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt) sa[kt] = sb[kt];
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  }  // tb < ntiles
 
   // ---- epilogue: O = O~ / l, lse ---------------------------------------------
   float llo, lhi;
   halves(st.l_run, llo, lhi);
   const float l_tot = llo + lhi;
-  const float inv = 1.0f / l_tot;
-  if (qi < N) {
+  // a row that saw no key (only possible within one key range of a split,
+  // or causal with more queries than keys): O = 0, lse = -inf
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (qi < Nq) {
+    const size_t head = qhead + split * p.o_split_stride;
     // O^T register r of row tile ct holds column 32ct + 8(r/4) + 4hh + r%4
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct)
@@ -498,8 +524,56 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         }
       }
     if (p.lse && hh == 0)
-      p.lse[static_cast<size_t>(bh) * N + qi] = (st.m_run + log2f(l_tot)) * kLn2;
+      p.lse[split * p.lse_split_stride + static_cast<size_t>(bh) * Nq + qi] =
+          l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
+}
+
+// ---- merge of key ranges -----------------------------------------------------
+//
+// Key range s of a query row left O_s = O~_s / l_s (fp32) and lse_s = m_s +
+// ln l_s (base e).  The two-block merge of the shakilmahmud.com page "Large
+// language models part 06: FlashAttention -- GPU SRAM, tiling, online
+// softmax", section 2, applied to all ranges at once: with m = max_s lse_s,
+//   l = sum_s exp(lse_s - m),  O = sum_s exp(lse_s - m) O_s / l,
+//   lse = m + ln l.
+// A range that saw no key of the row has lse_s = -inf and weight 0.
+template <int D, bool O32>
+__global__ __launch_bounds__(kThreads) void merge_splits_kernel(
+    const float *o_part, const float *lse_part, void *o, float *lse,
+    int64_t rows, int n_splits, size_t o_stride, size_t lse_stride) {
+  constexpr int LPR = 32;      // lanes per row
+  constexpr int CPL = D / LPR;  // columns per lane
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kThreads / LPR) +
+                      threadIdx.x / LPR;
+  const int col = (threadIdx.x % LPR) * CPL;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) m = fmaxf(m, lse_part[s * lse_stride + row]);
+  float acc[CPL], l = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float ls = lse_part[s * lse_stride + row];
+      if (ls == -INFINITY) continue;
+      const float w = __expf(ls - m);
+      l += w;
+      const float *src = o_part + s * o_stride + row * D + col;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = __builtin_fmaf(w, src[c], acc[c]);
+    }
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const size_t dst = static_cast<size_t>(row) * D + col;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    if (O32)
+      static_cast<float *>(o)[dst + c] = acc[c] * inv;
+    else
+      static_cast<__bf16 *>(o)[dst + c] = static_cast<__bf16>(acc[c] * inv);
+  }
+  if (lse && col == 0) lse[row] = l > 0.f ? m + __logf(l) : -INFINITY;
 }
 
 template <int D, bool CAUSAL, bool O32>
@@ -516,6 +590,23 @@ hipError_t launch_d(const Params &prm, bool causal, bool o32, hipStream_t s) {
   return o32 ? launch<D, false, true>(prm, s) : launch<D, false, false>(prm, s);
 }
 
+template <int D>
+hipError_t launch_merge(const FwdArgs &a, bool o32, size_t o_stride,
+                        size_t lse_stride, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(a.bh) * a.nq;
+  const int rpb = kThreads / 32;
+  const dim3 grid(static_cast<unsigned>((rows + rpb - 1) / rpb));
+  if (o32)
+    hipLaunchKernelGGL((merge_splits_kernel<D, true>), grid, dim3(kThreads), 0, s,
+                       a.o_part, a.lse_part, a.o, a.lse, rows, a.n_splits,
+                       o_stride, lse_stride);
+  else
+    hipLaunchKernelGGL((merge_splits_kernel<D, false>), grid, dim3(kThreads), 0, s,
+                       a.o_part, a.lse_part, a.o, a.lse, rows, a.n_splits,
+                       o_stride, lse_stride);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s) {
@@ -523,16 +614,34 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s) {
   prm.q = static_cast<const uint16_t *>(a.q);
   prm.k = static_cast<const uint16_t *>(a.k);
   prm.v = static_cast<const uint16_t *>(a.v);
-  prm.o = a.o;
-  prm.lse = a.lse;
-  prm.n = a.n;
+  prm.nq = a.nq;
+  prm.nk = a.nk;
   prm.h = a.h;
   prm.group = a.group;
-  prm.n_qblocks = (a.n + kRows - 1) / kRows;
-  prm.total = a.bh * prm.n_qblocks;
+  prm.n_qblocks = (a.nq + kRows - 1) / kRows;
+  prm.n_splits = a.n_splits;
+  const int bc = a.d == 128 ? Cfg<128>::BC : Cfg<64>::BC;
+  const int key_tiles = (a.nk + bc - 1) / bc;
+  prm.tiles_per_split = (key_tiles + a.n_splits - 1) / a.n_splits;
+  prm.total = a.bh * prm.n_qblocks * a.n_splits;
   prm.c = a.scale * kLog2e;
-  if (a.d == 128) return launch_d<128>(prm, a.causal, o32, s);
-  return launch_d<64>(prm, a.causal, o32, s);
+  if (a.n_splits == 1) {
+    prm.o = a.o;
+    prm.lse = a.lse;
+    prm.o_split_stride = prm.lse_split_stride = 0;
+    if (a.d == 128) return launch_d<128>(prm, a.causal, o32, s);
+    return launch_d<64>(prm, a.causal, o32, s);
+  }
+  // key ranges into the fp32 partial buffers, then the merge
+  prm.o = a.o_part;
+  prm.lse = a.lse_part;
+  prm.o_split_stride = static_cast<size_t>(a.bh) * a.nq * a.d;
+  prm.lse_split_stride = static_cast<size_t>(a.bh) * a.nq;
+  hipError_t e = a.d == 128 ? launch_d<128>(prm, a.causal, true, s)
+                            : launch_d<64>(prm, a.causal, true, s);
+  if (e != hipSuccess) return e;
+  return a.d == 128 ? launch_merge<128>(a, o32, prm.o_split_stride, prm.lse_split_stride, s)
+                    : launch_merge<64>(a, o32, prm.o_split_stride, prm.lse_split_stride, s);
 }
 
 }  // namespace fa2

@@ -134,8 +134,8 @@ hipError_t launch_fwd_fp32(const FwdArgs &a, hipStream_t s) {
   prm.v = static_cast<const float *>(a.v);
   prm.o = static_cast<float *>(a.o);
   prm.lse = a.lse;
-  prm.n = a.n;
-  prm.n_qblocks = (a.n + kRows - 1) / kRows;
+  prm.n = a.nq;  // the fp32 path has equal query and key lengths
+  prm.n_qblocks = (a.nq + kRows - 1) / kRows;
   prm.c = a.scale * kLog2e;
   const int grid = a.bh * prm.n_qblocks;
   if (a.d == 128)

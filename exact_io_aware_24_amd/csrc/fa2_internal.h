@@ -10,14 +10,18 @@ namespace fa2 {
 // Arguments shared by every forward kernel.  All pointers are device
 // pointers; shapes have been validated by the caller.
 struct FwdArgs {
-  const void *q;          // [B*H][N][d]
-  const void *k, *v;      // [B*H_kv][N][d]
-  void *o;                // [B*H][N][d]
-  float *lse;             // [B*H][N] or nullptr
+  const void *q;          // [B*H][Nq][d]
+  const void *k, *v;      // [B*H_kv][Nk][d]
+  void *o;                // [B*H][Nq][d]
+  float *lse;             // [B*H][Nq] or nullptr
   int bh;                 // B*H
   int h;                  // H, query heads per batch index
   int group;              // H / H_kv, query heads per K/V head (1: none shared)
-  int n;                  // sequence length
+  int nq;                 // query rows per head
+  int nk;                 // key rows per head
+  int n_splits;           // key ranges computed separately, then merged
+  float *o_part;          // [n_splits][B*H][Nq][d] fp32 (n_splits > 1)
+  float *lse_part;        // [n_splits][B*H][Nq] fp32 (n_splits > 1)
   int d;                  // head dimension (64 or 128)
   float scale;            // multiplies q.k
   bool causal;

@@ -42,6 +42,7 @@ class Workload:
     dtype: str  # "bf16" or "fp32": the type Q, K, V are stored in
     outliers: bool = False  # 5 % of Q and K rows scaled by 20
     H_kv: int = 0  # K/V heads (grouped-query attention); 0 means H
+    Nq: int = 0    # query rows when they differ from the N keys; 0 means N
 
     @property
     def scale(self) -> float:
@@ -49,18 +50,23 @@ class Workload:
 
     @property
     def flops(self) -> float:
-        """Algorithmic FLOPs, 4*B*H*N^2*d, halved when causal."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        """Algorithmic FLOPs, 4*B*H*Nq*N*d, halved when causal (square)."""
+        f = 4.0 * self.B * self.H * self.q_rows * self.N * self.d
         return f / 2 if self.causal else f
 
     @property
     def kv_heads(self) -> int:
         return self.H_kv or self.H
 
+    @property
+    def q_rows(self) -> int:
+        return self.Nq or self.N
+
     def describe(self) -> str:
-        return "B=%d,H=%d%s,N=%d,d=%d,%s,%s%s" % (
+        return "B=%d,H=%d%s,%sN=%d,d=%d,%s,%s%s" % (
             self.B, self.H,
             (",H_kv=%d" % self.kv_heads) if self.kv_heads != self.H else "",
+            ("Nq=%d," % self.q_rows) if self.q_rows != self.N else "",
             self.N, self.d,
             "causal" if self.causal else "non-causal", self.dtype,
             ",5%-rows-x20-outliers" if self.outliers else "")
@@ -80,28 +86,32 @@ WORKLOADS = {
         # K/V head
         Workload("gqa_causal_b2h16kv2_n8192_d128", 2, 16, 8192, 128, True,
                  "bf16", H_kv=2),
+        # decoding one token against a 16384-entry key/value cache
+        Workload("decode_b8h32_nq1_nk16384_d128", 8, 32, 16384, 128, False,
+                 "bf16", Nq=1),
     ]
 }
 HEADLINE = "causal_b2h16_n8192_d128"
 
 
 def make_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16",
-                seed: int = DEFAULT_SEED, outliers: bool = False, H_kv: int = 0):
-    """Return CPU tensors ``(q, k, v)``: q ``[B, H, N, d]``, k and v
-    ``[B, H_kv, N, d]`` (``H_kv`` = 0 means H)."""
+                seed: int = DEFAULT_SEED, outliers: bool = False, H_kv: int = 0,
+                Nq: int = 0):
+    """Return CPU tensors ``(q, k, v)``: q ``[B, H, Nq, d]``, k and v
+    ``[B, H_kv, N, d]`` (``H_kv`` = 0 means H, ``Nq`` = 0 means N)."""
     if dtype not in ("bf16", "fp32"):
         raise ValueError("dtype must be 'bf16' or 'fp32'")
     hk = H_kv or H
     g = torch.Generator(device="cpu").manual_seed(int(seed))
-    q = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    q = torch.randn(B, H, Nq or N, d, generator=g, dtype=torch.float32)
     k = torch.randn(B, hk, N, d, generator=g, dtype=torch.float32)
     v = torch.randn(B, hk, N, d, generator=g, dtype=torch.float32)
     if outliers:
-        n_out = int(math.floor(0.05 * N))
         for t in (q, k):
+            n_out = int(math.floor(0.05 * t.shape[2]))
             for b in range(B):
                 for h in range(t.shape[1]):
-                    rows = torch.randperm(N, generator=g)[:n_out]
+                    rows = torch.randperm(t.shape[2], generator=g)[:n_out]
                     t[b, h, rows] *= 20.0
     if dtype == "bf16":
         q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
@@ -118,4 +128,4 @@ def make_dout(B: int, H: int, N: int, d: int, seed: int = DEFAULT_SEED + 1):
 def workload_inputs(w: Workload, seed: int = DEFAULT_SEED):
     """Inputs of a named workload (CPU tensors)."""
     return make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed=seed,
-                       outliers=w.outliers, H_kv=w.H_kv)
+                       outliers=w.outliers, H_kv=w.H_kv, Nq=w.Nq)

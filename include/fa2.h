@@ -74,6 +74,8 @@ extern "C" {
    <= 2^31 - 1 for fa2_fwd_fp32. */
 #define FA2_MAX_ELEMS (1LL << 40)
 #define FA2_MAX_HEAD_ELEMS_BF16 ((1LL << 30) - (1LL << 16))
+/* Largest n_splits of fa2_fwd_splitkv. */
+#define FA2_MAX_SPLITS 1024
 
 /*
  * fa2_fwd -- bf16 inputs, bf16 output.
@@ -120,6 +122,44 @@ int fa2_fwd_gqa(const void *q, const void *k, const void *v, void *o,
 int fa2_fwd_gqa_o32(const void *q, const void *k, const void *v, float *o,
                     float *lse, int B, int H, int H_kv, int N, int d,
                     float scale, int causal, void *stream);
+
+/*
+ * fa2_fwd_splitkv -- the general forward: Nq query rows against Nk keys
+ * (decoding against a key/value cache, chunked prefill), grouped K/V heads,
+ * and the keys of each query block optionally split into n_splits ranges
+ * computed by separate workgroups and then merged.  Splitting fills the GPU
+ * when B * H * ceil(Nq / 128) alone would give too few workgroups.  The
+ * merge is the two-block online-softmax merge of the shakilmahmud.com page
+ * "Large language models part 06: FlashAttention -- GPU SRAM, tiling,
+ * online softmax", section 2, over all ranges of a row.
+ *   q, o     : [B][H][Nq][d] (o bf16);  k, v : const bf16 [B][H_kv][Nk][d]
+ *   lse      : float [B][H][Nq] or NULL
+ *   Nq, Nk   : >= 1 each
+ *   causal   : query i sits at key position i + Nk - Nq and sees the keys
+ *              at or before it (the last query sees every key; Nq == Nk is
+ *              fa2_fwd's mask).  A query that sees no key (only when
+ *              Nq > Nk) gets O = 0 and lse = -inf.
+ *   n_splits : 1 .. FA2_MAX_SPLITS; with 1, o_part and lse_part are unused
+ *              (may be NULL) and the call is one kernel launch
+ *   o_part   : float [n_splits][B][H][Nq][d] caller-owned workspace
+ *   lse_part : float [n_splits][B][H][Nq] caller-owned workspace
+ * Range s covers key tiles [s*T, (s+1)*T) with T = ceil(ceil(Nk/BC) /
+ * n_splits) (BC = 64 keys at d = 128, 128 at d = 64); ranges past the end
+ * are empty and contribute nothing.  The workspaces must not overlap any
+ * input, output or each other (FA2_ERR_ALIAS); n_splits outside its range or
+ * a grid over 2^31 - 1 workgroups is FA2_ERR_SHAPE.  Results depend on
+ * n_splits only through fp32 rounding in the merge.
+ */
+int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
+                    float *lse, int B, int H, int H_kv, int Nq, int Nk, int d,
+                    float scale, int causal, int n_splits, float *o_part,
+                    float *lse_part, void *stream);
+
+/* fa2_fwd_splitkv_o32 -- fa2_fwd_splitkv with a float [B][H][Nq][d] o. */
+int fa2_fwd_splitkv_o32(const void *q, const void *k, const void *v, float *o,
+                        float *lse, int B, int H, int H_kv, int Nq, int Nk,
+                        int d, float scale, int causal, int n_splits,
+                        float *o_part, float *lse_part, void *stream);
 
 /*
  * fa2_fwd_fp32 -- float32 q, k, v and o; every step (scores, softmax,
@@ -169,7 +209,8 @@ int fa2_bwd_o32(const void *q, const void *k, const void *v, const void *o,
 /* Static English description of a return code (never NULL). */
 const char *fa2_strerror(int code);
 
-/* Library ABI version: 3 (2 added the backward pass, 3 grouped K/V heads). */
+/* Library ABI version: 4 (2 added the backward pass, 3 grouped K/V heads,
+   4 split key ranges with separate query and key lengths). */
 int fa2_version(void);
 
 #ifdef __cplusplus

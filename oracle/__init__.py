@@ -246,6 +246,31 @@ def expand_kv_heads(kv, heads: int):
     return np.repeat(kv, heads // hk, axis=-3)
 
 
+def attention_offset(q, k, v, scale: float, causal: bool = False,
+                     nthreads: int = 0):
+    """Exact attention of ``q`` ``[..., Nq, d]`` against ``k, v``
+    ``[..., Nk, d]`` (same heads) with the causal mask aligned at the end of
+    the keys: query i is at key position ``i + Nk - Nq`` and sees the keys at
+    or before it -- the rows ``Nk - Nq .. Nk - 1`` of the square problem
+    over all Nk positions.  Rows with no visible key get O = 0, lse = -inf.
+    Returns ``(o, lse, threads_used)``."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    nq, nk, d = q.shape[-2], k.shape[-2], q.shape[-1]
+    if not causal or nq == nk:
+        return attention(q, k, v, scale, causal, nthreads)
+    lead = q.shape[:-2]
+    qh = q.reshape(-1, nq, d)
+    kh, vh = k.reshape(-1, nk, d), v.reshape(-1, nk, d)
+    rows = np.arange(nq, dtype=np.int64) + (nk - nq)
+    o = np.empty(qh.shape)
+    lse = np.empty(qh.shape[:2])
+    used = 0
+    for h in range(qh.shape[0]):
+        o[h], lse[h], used = attention_rows(qh[h], rows, kh[h], vh[h], scale,
+                                            True, nthreads)
+    return o.reshape(lead + (nq, d)), lse.reshape(lead + (nq,)), used
+
+
 def attention_gqa(q, k, v, scale: float, causal: bool = False, nthreads: int = 0):
     """Exact attention with grouped K/V heads: ``q`` ``[..., H, N, d]``,
     ``k``, ``v`` ``[..., H_kv, N, d]`` (H_kv dividing H).  Returns

@@ -314,6 +314,34 @@ def pin_gqa_head_map(orc):
     assert np.array_equal(orc_mod.expand_kv_heads(k2, H), k2)
 
 
+def pin_offset_causal(orc):
+    """Causal mask with more keys than queries (query i at key position
+    i + Nk - Nq): with Nq = Nk it is the plain causal mask; the last query
+    sees every key (equals the unmasked row); rows before the first key
+    position see nothing (O = 0, lse = -inf); and each row equals the
+    brute-force softmax over its visible keys."""
+    import oracle as orc_mod
+    r = _rng(31)
+    q = r.standard_normal((2, 7, 5))
+    k = r.standard_normal((2, 11, 5))
+    v = r.standard_normal((2, 11, 5))
+    o, lse, _ = orc_mod.attention_offset(q, k, v, 0.6, True)
+    ou, lu, _ = orc.attention(q, k, v, 0.6, False)
+    _close(o[:, -1], ou[:, -1], what="last row")
+    _close(lse[:, -1], lu[:, -1], what="last lse")
+    for h in range(2):
+        for i in range(7):
+            vis = 11 - 7 + i + 1
+            s = 0.6 * k[h, :vis] @ q[h, i]
+            w = np.exp(s - s.max())
+            _close(o[h, i], (w / w.sum()) @ v[h, :vis], what="row %d" % i)
+    sq, _, _ = orc_mod.attention_offset(q, k[:, :7], v[:, :7], 0.6, True)
+    sq2, _, _ = orc.attention(q, k[:, :7], v[:, :7], 0.6, True)
+    _close(sq, sq2, tol=0, what="square")
+    o3, l3, _ = orc_mod.attention_offset(k, q, q, 0.6, True)  # 11 queries, 7 keys
+    assert np.all(o3[:, :4] == 0) and np.all(np.isneginf(l3[:, :4]))
+
+
 # ---------------------------------------------------------------------------
 # gradients
 
@@ -464,6 +492,7 @@ ALL_PINS = [
     pin_brute_force,
     pin_rows_match_full,
     pin_gqa_head_map,
+    pin_offset_causal,
     pin_bwd_finite_differences,
     pin_bwd_sums,
     pin_bwd_constant_v,

@@ -50,7 +50,7 @@ def test_codes_match_header():
 
 
 def test_version_and_strerror(L):
-    assert fa2.version() == 3
+    assert fa2.version() == 4
     seen = set()
     for name, code in header_codes().items():
         msg = fa2.strerror(code)
@@ -210,3 +210,46 @@ def test_gqa_validation(L, fn):
     # (1*2*64*64 bf16 = 16 KiB) is fine only if it does not overlap
     assert call_gqa(fn, o=GOOD["k"] + 16 * 1024 - 16) == fa2.FA2_ERR_ALIAS
     assert call_gqa(fn, lse=GOOD["v"] + 4096) == fa2.FA2_ERR_ALIAS
+
+
+# Split-KV forward: separate query / key lengths, key ranges + merge
+SPLIT_FUNCS = ("fa2_fwd_splitkv", "fa2_fwd_splitkv_o32")
+SPLIT_NAMES = ("q", "k", "v", "o", "lse", "o_part", "lse_part")
+SPLIT_GOOD = {n: 0x10000000 + i * 64 * MiB for i, n in enumerate(SPLIT_NAMES)}
+
+
+def call_split(fn, ptrs=None, B=1, H=4, H_kv=2, Nq=16, Nk=1000, d=128,
+               scale=0.1, causal=1, n_splits=4):
+    p = dict(SPLIT_GOOD)
+    p.update(ptrs or {})
+    return fa2.raw_call_splitkv(fn, [p[n] for n in SPLIT_NAMES], B, H, H_kv, Nq,
+                                Nk, d, scale, causal, n_splits)
+
+
+@pytest.mark.parametrize("fn", SPLIT_FUNCS)
+def test_splitkv_validation(L, fn):
+    for kw in (dict(Nq=0), dict(Nk=0), dict(H_kv=3), dict(n_splits=0),
+               dict(n_splits=-2), dict(n_splits=fa2.MAX_SPLITS + 1),
+               dict(B=1 << 14, H=1 << 14, Nq=1 << 10, n_splits=1000)):
+        assert call_split(fn, **kw) == fa2.FA2_ERR_SHAPE, kw
+    for name in ("q", "k", "v", "o", "o_part", "lse_part"):
+        assert call_split(fn, {name: None}) == fa2.FA2_ERR_NULL, name
+    assert call_split(fn, d=80) == fa2.FA2_ERR_HEADDIM
+    assert call_split(fn, scale=float("inf")) == fa2.FA2_ERR_SCALE
+    for name in SPLIT_NAMES:
+        assert call_split(fn, {name: SPLIT_GOOD[name] + 4}) == fa2.FA2_ERR_ALIGN, name
+    # workspaces against every input and output, and against each other
+    for part in ("o_part", "lse_part"):
+        for other in ("q", "k", "v", "o", "lse"):
+            assert call_split(fn, {part: SPLIT_GOOD[other] + 16}) == fa2.FA2_ERR_ALIAS, (part, other)
+    assert call_split(fn, {"lse_part": SPLIT_GOOD["o_part"] + 64}) == fa2.FA2_ERR_ALIAS
+
+
+def test_default_splits():
+    # decode: one query block per head -> split up to ~1024 workgroups
+    assert fa2.default_splits(8, 32, 1, 16384, 128) == 4
+    assert fa2.default_splits(1, 1, 1, 65536, 128) == 256
+    # short keys: never below four tiles per range
+    assert fa2.default_splits(1, 1, 1, 300, 128) == 1
+    # already enough workgroups: no split
+    assert fa2.default_splits(2, 16, 8192, 8192, 128) == 1

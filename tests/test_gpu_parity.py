@@ -125,7 +125,8 @@ def sample_rows(N, rng, extra=24):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-BIG = [n for n in wl.WORKLOADS if n != "tiny_fp32_n128_d64"]
+BIG = [n for n, w in wl.WORKLOADS.items()
+       if w.dtype == "bf16" and w.q_rows == w.N]
 
 
 @pytest.mark.parametrize("name", BIG)
