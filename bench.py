@@ -189,6 +189,8 @@ def main(argv=None):
                     help="entry point to time (o32: fp32 outputs)")
     ap.add_argument("--seq-len", type=int, default=0,
                     help="override the workload's sequence length")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="key ranges for fa2_fwd_splitkv workloads (0: the default)")
     ap.add_argument("--per-call", action="store_true",
                     help="also time single calls (median, min)")
     ap.add_argument("--cold-mall", type=int, default=0, metavar="MIB",
@@ -246,7 +248,7 @@ def main(argv=None):
     if decode:
         flops = w.flops
         entry = "fa2_fwd_splitkv"
-        n_splits = fa2.default_splits(w.B, w.H, w.q_rows, w.N, w.d)
+        n_splits = args.splits or fa2.default_splits(w.B, w.H, w.q_rows, w.N, w.d)
         o = torch.empty(qd.shape, dtype=out_dtype, device=dev)
         o_part = torch.empty((n_splits,) + tuple(qd.shape), dtype=torch.float32, device=dev)
         lse_part = torch.empty((n_splits,) + tuple(qd.shape[:3]), dtype=torch.float32,
@@ -316,7 +318,8 @@ def main(argv=None):
                     "median_tflops": round(flops / (per[len(per) // 2] * 1e-3) / 1e12, 3),
                     "cold_mall_mib": args.cold_mall}
 
-    same_shape = not args.seq_len and entry == "fa2_" + args.which
+    default_entry = "fa2_fwd_splitkv" if decode else "fa2_" + args.which
+    same_shape = not args.seq_len and not args.splits and entry == default_entry
     traffic = read_traffic(name, args.which) if same_shape else None
     comp = compulsory_bytes(w.B, w.H, w.N, w.d, Nq=w.q_rows, H_kv=w.kv_heads)
     if decode:  # bandwidth-bound: K and V are read once, little arithmetic
