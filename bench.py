@@ -12,6 +12,9 @@ counted at the usual 2.5x the forward's flop: the five products S, dP, dV,
 dK, dQ.  Workloads with fewer query rows than keys (decoding) run through
 ``fa2_fwd_splitkv`` with its default key-range split and are reported
 against the HBM roofline (their bytes: K, V, Q read, O and lse written).
+``--entry fa2_fwd_fp8`` times the FP8 attention on inputs quantised (with
+the random-sign rotation of Q and K) before the timed region, against the
+fp8 MFMA peak; the quantisation time of Q, K and V is reported beside it.
 W untimed warm-up steps are followed by exactly K timed steps between HIP
 events on the stream the kernel is launched on.  Rank 0 prints one JSON line:
 TFLOP/s (4*B*H*N^2*d, halved for causal), the roofline of the kernel against
@@ -43,6 +46,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 CSRC = os.path.join(ROOT, "exact_io_aware_24_amd", "csrc")
 KERNEL_SRCS = {"fwd": ("fa2_fwd_bf16.hip", "fa2_device.h"),
                "bwd": ("fa2_bwd_bf16.hip", "fa2_device.h")}
@@ -185,7 +189,8 @@ def main(argv=None):
     ap.add_argument("--pass", dest="which", default="fwd", choices=("fwd", "bwd"),
                     help="forward (fa2_fwd) or backward (fa2_bwd) pass")
     ap.add_argument("--entry", default=None,
-                    choices=("fa2_fwd", "fa2_fwd_o32", "fa2_bwd", "fa2_bwd_o32"),
+                    choices=("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_fp8", "fa2_bwd",
+                             "fa2_bwd_o32"),
                     help="entry point to time (o32: fp32 outputs)")
     ap.add_argument("--seq-len", type=int, default=0,
                     help="override the workload's sequence length")
@@ -235,6 +240,10 @@ def main(argv=None):
         print("the backward pass takes one K/V head per query head", file=sys.stderr)
         return 2
     decode = w.q_rows != w.N
+    if entry == "fa2_fwd_fp8" and (decode or w.kv_heads != w.H):
+        print("fa2_fwd_fp8 takes equal query and key lengths and one K/V head per "
+              "query head", file=sys.stderr)
+        return 2
     if decode and (args.which == "bwd" or entry != "fa2_fwd" or args.seq_len):
         print("workloads with fewer queries than keys time fa2_fwd_splitkv only",
               file=sys.stderr)
@@ -245,7 +254,32 @@ def main(argv=None):
     out_dtype = torch.float32 if entry.endswith("_o32") else torch.bfloat16
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
     n_splits = None
-    if decode:
+    fp8 = entry == "fa2_fwd_fp8"
+    quant_ms = None
+    if fp8:
+        flops = w.flops
+        signs = wl.make_signs(w.d).to(dev)
+        o = torch.empty(qd.shape, dtype=torch.bfloat16, device=dev)
+
+        def quantize():
+            return (fa2.quantize_fp8(qd, 128, signs), fa2.quantize_fp8(kd, 64, signs),
+                    fa2.quantize_fp8(vd, 64, None))
+        (q8, qe), (k8, ke), (v8, ve) = quantize()
+        for _ in range(20):
+            quantize()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            quantize()
+        e1.record()
+        torch.cuda.synchronize()
+        quant_ms = e0.elapsed_time(e1) / 50
+
+        def step():
+            fa2.forward_fp8(q8, qe, k8, ke, v8, ve, causal=w.causal, scale=w.scale,
+                            rotated=True, out=o, lse=lse)
+    elif decode:
         flops = w.flops
         entry = "fa2_fwd_splitkv"
         n_splits = args.splits or fa2.default_splits(w.B, w.H, w.q_rows, w.N, w.d)
@@ -328,9 +362,10 @@ def main(argv=None):
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                     "traffic": traffic}
     else:
+        peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
         roofline = {"bound": "mfma", "achieved": round(tflops, 3),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+                    "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4), "traffic": traffic}
     rec = {
         "metric": "attention %s TFLOP/s (1 MI355X) and %% of bf16 MFMA peak" % args.which,
         "value": round(tflops, 3),
@@ -342,7 +377,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3" if fp8 else "bf16",
         "data": "synthetic (seeded randn, bf16)",
         "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads,
                    "Nq": w.q_rows, "N": w.N, "d": w.d, "causal": w.causal,
@@ -357,6 +392,8 @@ def main(argv=None):
     }
     if per_call is not None:
         rec["per_call"] = per_call
+    if quant_ms is not None:
+        rec["fp8_quantize_ms"] = round(quant_ms, 5)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = (cpu_baseline(w, q, k, v, args.cpu_budget)
                                if args.which == "fwd" else

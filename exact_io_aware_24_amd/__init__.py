@@ -31,7 +31,8 @@ FA2_ERR_HIP = -7
 
 # Every symbol include/fa2.h declares.
 EXPORTED = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_gqa", "fa2_fwd_gqa_o32",
-            "fa2_fwd_splitkv", "fa2_fwd_splitkv_o32", "fa2_fwd_fp32", "fa2_bwd",
+            "fa2_fwd_splitkv", "fa2_fwd_splitkv_o32", "fa2_quantize_fp8",
+            "fa2_fwd_fp8", "fa2_fwd_fp8_o32", "fa2_fwd_fp32", "fa2_bwd",
             "fa2_bwd_o32", "fa2_strerror", "fa2_version")
 MAX_SPLITS = 1024  # FA2_MAX_SPLITS
 
@@ -73,6 +74,12 @@ def lib() -> ctypes.CDLL:
         for name in ("fa2_fwd_splitkv", "fa2_fwd_splitkv_o32"):
             f = getattr(L, name)
             f.argtypes = ssig
+            f.restype = ctypes.c_int
+        L.fa2_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp]
+        L.fa2_quantize_fp8.restype = ctypes.c_int
+        for name in ("fa2_fwd_fp8", "fa2_fwd_fp8_o32"):
+            f = getattr(L, name)
+            f.argtypes = [vp] * 8 + [i, i, i, i, ctypes.c_float, i, i, vp]
             f.restype = ctypes.c_int
         bsig = [vp] * 10 + [i, i, i, i, ctypes.c_float, i, vp]
         for name in ("fa2_bwd", "fa2_bwd_o32"):
@@ -331,6 +338,83 @@ def raw_call_splitkv(fn: str, ptrs, B, H, H_kv, Nq, Nk, d, scale, causal,
     return int(getattr(lib(), fn)(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d,
                                   ctypes.c_float(scale), int(causal), n_splits,
                                   op, lp, stream))
+
+
+def quantize_fp8(x, block_rows: int, signs=None, codes=None, exps=None):
+    """Block-quantise a contiguous bfloat16 GPU tensor ``[B, H, N, d]`` to
+    e4m3 codes (``fa2_quantize_fp8``), optionally rotating each row by the
+    random-sign Walsh-Hadamard transform given by ``signs`` (a float32 GPU
+    tensor of d values +-1).  Returns ``(codes uint8 [B, H, N, d], exps int32
+    [B, H, ceil(N / block_rows)])``."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dim() != 4 or not x.is_cuda \
+            or not x.is_contiguous() or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a contiguous bfloat16 GPU tensor [B, H, N, d]")
+    B, H, N, d = (int(v) for v in x.shape)
+    nb = -(-N // block_rows)
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if exps is None:
+        exps = torch.empty((B, H, nb), dtype=torch.int32, device=x.device)
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d
+                              or not signs.is_cuda):
+        raise ValueError("signs must be a float32 GPU tensor of d values")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib().fa2_quantize_fp8(x.data_ptr(), codes.data_ptr(), exps.data_ptr(),
+                                    B, H, N, d, int(block_rows),
+                                    signs.data_ptr() if signs is not None else None,
+                                    stream)
+    if rc != FA2_OK:
+        raise FA2Error(rc, "fa2_quantize_fp8")
+    return codes, exps
+
+
+def forward_fp8(q8, q_exp, k8, k_exp, v8, v_exp, causal: bool = False,
+                scale: float | None = None, rotated: bool = False,
+                out_dtype=None, out=None, lse=None):
+    """FP8 attention (``fa2_fwd_fp8[_o32]``) of quantised inputs from
+    :func:`quantize_fp8` (Q with 128-row blocks, K and V with 64-row blocks,
+    Q and K rotated with the same signs iff ``rotated``).  ``scale`` is the
+    attention scale of the original inputs (default 1/sqrt(d)).  Returns
+    ``(o, lse)``."""
+    import torch
+    B, H, N, d = (int(v) for v in q8.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    odt = torch.bfloat16 if out_dtype is None else out_dtype
+    fn = {torch.bfloat16: "fa2_fwd_fp8", torch.float32: "fa2_fwd_fp8_o32"}.get(odt)
+    if fn is None:
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (B, H, N, d) or not t.is_cuda \
+                or not t.is_contiguous():
+            raise ValueError("codes must be contiguous uint8 GPU tensors [B, H, N, d]")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=odt, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    with torch.cuda.device(q8.device):
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+        rc = getattr(lib(), fn)(q8.data_ptr(), q_exp.data_ptr(), k8.data_ptr(),
+                                k_exp.data_ptr(), v8.data_ptr(), v_exp.data_ptr(),
+                                out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                                ctypes.c_float(scale), int(bool(rotated)),
+                                int(bool(causal)), stream)
+    if rc != FA2_OK:
+        raise FA2Error(rc, fn)
+    return out, lse
+
+
+def attention_fp8(q, k, v, causal: bool = False, scale: float | None = None,
+                  signs=None, out_dtype=None):
+    """bf16 ``q, k, v`` -> FP8 attention: quantise (Q and K rotated by
+    ``signs`` when given), then :func:`forward_fp8`.  Returns ``(o, lse)``."""
+    q8, qe = quantize_fp8(q, 128, signs)
+    k8, ke = quantize_fp8(k, 64, signs)
+    v8, ve = quantize_fp8(v, 64, None)
+    return forward_fp8(q8, qe, k8, ke, v8, ve, causal=causal, scale=scale,
+                       rotated=signs is not None, out_dtype=out_dtype)
 
 
 def raw_call_bwd(fn: str, ptrs, B, H, N, d, scale, causal, stream=None) -> int:

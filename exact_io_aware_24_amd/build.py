@@ -22,7 +22,8 @@ LIB_NAME = "libfa2.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_fp32.hip", "fa2_bwd_bf16.hip"]
+SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_fp32.hip", "fa2_bwd_bf16.hip",
+           "fa2_fp8.hip"]
 
 
 def hipcc() -> str:

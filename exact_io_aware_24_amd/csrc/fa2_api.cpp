@@ -250,6 +250,91 @@ FA2_EXPORT int fa2_fwd_splitkv_o32(const void *q, const void *k, const void *v,
                  n_splits, o_part, lse_part, true, stream);
 }
 
+FA2_EXPORT int fa2_quantize_fp8(const void *x, void *codes, int *exps, int B,
+                                int H, int N, int d, int block_rows,
+                                const float *signs, void *stream) {
+  if (!x || !codes || !exps) return FA2_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1 || (block_rows != 64 && block_rows != 128))
+    return FA2_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
+  const int64_t bh = static_cast<int64_t>(B) * H;
+  const int64_t nb = (static_cast<int64_t>(N) + block_rows - 1) / block_rows;
+  if (bh * nb > INT32_MAX || bh * N * d > FA2_MAX_ELEMS) return FA2_ERR_SHAPE;
+  if (misaligned(x) || misaligned(codes) || (reinterpret_cast<uintptr_t>(exps) & 3) ||
+      (signs && (reinterpret_cast<uintptr_t>(signs) & 3)))
+    return FA2_ERR_ALIGN;
+  const int64_t elems = bh * N * d;
+  const Range rx = span(x, elems * 2), rc = span(codes, elems),
+              re = span(exps, bh * nb * 4), rs = span(signs, signs ? d * 4 : 0);
+  if (overlaps(rc, rx) || overlaps(rc, re) || overlaps(rc, rs) ||
+      overlaps(re, rx) || overlaps(re, rs))
+    return FA2_ERR_ALIAS;
+  fa2::QuantArgs a;
+  a.x = x;
+  a.codes = codes;
+  a.exps = exps;
+  a.signs = signs;
+  a.bh = static_cast<int>(bh);
+  a.n = N;
+  a.d = d;
+  a.block_rows = block_rows;
+  return finish(fa2::launch_quantize_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
+static int fwd_fp8(const void *q8, const int *qe, const void *k8, const int *ke,
+                   const void *v8, const int *ve, void *o, float *lse, int B,
+                   int H, int N, int d, float scale, int rotated, int causal,
+                   bool o32, void *stream) {
+  if (!qe || !ke || !ve) return FA2_ERR_NULL;
+  // shapes, scale, alignment and aliasing of q, k, v, o, lse (1-byte codes)
+  int rc = validate(q8, k8, v8, o, lse, B, H, H, N, N, d, scale, 1, o32 ? 4 : 2,
+                    fa2::kFp8RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc != FA2_OK) return rc;
+  if ((reinterpret_cast<uintptr_t>(qe) | reinterpret_cast<uintptr_t>(ke) |
+       reinterpret_cast<uintptr_t>(ve)) & 3)
+    return FA2_ERR_ALIGN;
+  const int64_t bh = static_cast<int64_t>(B) * H;
+  const int64_t rows = bh * N;
+  const Range out[2] = {span(o, rows * d * (o32 ? 4 : 2)), span(lse, lse ? rows * 4 : 0)};
+  const Range ex[3] = {span(qe, bh * ((N + 127) / 128) * 4), span(ke, bh * ((N + 63) / 64) * 4),
+                       span(ve, bh * ((N + 63) / 64) * 4)};
+  for (const Range &r : out)
+    for (const Range &e : ex)
+      if (overlaps(r, e)) return FA2_ERR_ALIAS;
+  fa2::Fp8Args a;
+  a.q = q8;
+  a.k = k8;
+  a.v = v8;
+  a.qe = qe;
+  a.ke = ke;
+  a.ve = ve;
+  a.o = o;
+  a.lse = lse;
+  a.bh = static_cast<int>(bh);
+  a.n = N;
+  a.d = d;
+  a.scale = rotated ? scale / static_cast<float>(d) : scale;
+  a.causal = causal != 0;
+  return finish(fa2::launch_fwd_fp8(a, o32, static_cast<hipStream_t>(stream)));
+}
+
+FA2_EXPORT int fa2_fwd_fp8(const void *q8, const int *q_exp, const void *k8,
+                           const int *k_exp, const void *v8, const int *v_exp,
+                           void *o, float *lse, int B, int H, int N, int d,
+                           float scale, int rotated, int causal, void *stream) {
+  return fwd_fp8(q8, q_exp, k8, k_exp, v8, v_exp, o, lse, B, H, N, d, scale,
+                 rotated, causal, false, stream);
+}
+
+FA2_EXPORT int fa2_fwd_fp8_o32(const void *q8, const int *q_exp, const void *k8,
+                               const int *k_exp, const void *v8,
+                               const int *v_exp, float *o, float *lse, int B,
+                               int H, int N, int d, float scale, int rotated,
+                               int causal, void *stream) {
+  return fwd_fp8(q8, q_exp, k8, k_exp, v8, v_exp, o, lse, B, H, N, d, scale,
+                 rotated, causal, true, stream);
+}
+
 FA2_EXPORT int fa2_fwd_fp32(const float *q, const float *k, const float *v,
                             float *o, float *lse, int B, int H, int N, int d,
                             float scale, int causal, void *stream) {
@@ -304,4 +389,4 @@ FA2_EXPORT const char *fa2_strerror(int code) {
   }
 }
 
-FA2_EXPORT int fa2_version(void) { return 4; }
+FA2_EXPORT int fa2_version(void) { return 5; }

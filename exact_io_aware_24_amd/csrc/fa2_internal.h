@@ -49,9 +49,34 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, bool o32, hipStream_t s);
 // fp32 q/k/v/o, fp32 arithmetic throughout.
 hipError_t launch_fwd_fp32(const FwdArgs &a, hipStream_t s);
 
+// FP8 block quantisation of one bf16 tensor [B*H][N][d].
+struct QuantArgs {
+  const void *x;       // bf16
+  void *codes;         // e4m3 codes, same layout
+  int *exps;           // [B*H][ceil(N / block_rows)] block exponents
+  const float *signs;  // [d] +-1 (rotation) or nullptr
+  int bh, n, d, block_rows;
+};
+hipError_t launch_quantize_fp8(const QuantArgs &a, hipStream_t s);
+
+// FP8 attention on quantised Q (128-row blocks), K and V (64-row blocks).
+struct Fp8Args {
+  const void *q, *k, *v;     // e4m3 codes [B*H][N][d]
+  const int *qe, *ke, *ve;   // block exponents
+  void *o;                   // bf16 or fp32 [B*H][N][d]
+  float *lse;                // [B*H][N] or nullptr
+  int bh, n, d;
+  float scale;               // already divided by d for rotated Q, K
+  bool causal;
+};
+hipError_t launch_fwd_fp8(const Fp8Args &a, bool o32, hipStream_t s);
+
 // Query rows per workgroup of each kernel (the grid is B*H*ceil(N/rows)).
 constexpr int kBf16RowsPerBlock = 128;
 constexpr int kFp32RowsPerBlock = 64;
+// FP8 path: Q blocks of 128 rows, K/V tiles of 64 rows (one exponent each).
+constexpr int kFp8RowsPerBlock = 128;
+constexpr int kFp8KvRowsPerBlock = 64;
 // Rows (queries or keys) per workgroup of the backward kernels.
 constexpr int kBf16BwdRowsPerBlock = 128;
 

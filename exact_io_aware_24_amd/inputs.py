@@ -118,6 +118,13 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str = "bf16",
     return q, k, v
 
 
+def make_signs(d: int, seed: int = DEFAULT_SEED + 2):
+    """Random +-1 signs (float32, CPU) of the FP8 path's incoherent
+    processing rotation diag(signs) H / sqrt(d)."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    return (torch.randint(0, 2, (d,), generator=g) * 2 - 1).to(torch.float32)
+
+
 def make_dout(B: int, H: int, N: int, d: int, seed: int = DEFAULT_SEED + 1):
     """An incoming gradient of the output for the backward pass: bf16 CPU
     tensor ``[B, H, N, d]`` of seeded standard normal values."""

@@ -162,6 +162,47 @@ int fa2_fwd_splitkv_o32(const void *q, const void *k, const void *v, float *o,
                         float *o_part, float *lse_part, void *stream);
 
 /*
+ * FP8 path: block quantisation with incoherent processing (the FP8 recipe
+ * of FlashAttention-3 on the itimpress.au page "FlashAttention scaling,
+ * multi-GPU training and weight quantisation", section 1: small tiles
+ * scaled independently; Q and K multiplied by a random orthogonal matrix
+ * before quantising to spread outliers), then attention on the gfx950 FP8
+ * MFMA.  Codes are OCP e4m3 (bias 7, max 448, round to nearest even).
+ *
+ * fa2_quantize_fp8 -- x: const bf16 [B][H][N][d]; codes: e4m3 [B][H][N][d]
+ * (written); exps: int [B][H][ceil(N / block_rows)] (written).  With signs
+ * (device float [d] of +-1, or NULL for no rotation) each row is multiplied
+ * by the signs and transformed by the unnormalised Walsh-Hadamard transform
+ * (fp32 add/sub butterflies, stages h = 1, 2, 4, ...), i.e. rotated by
+ * diag(signs) H / sqrt(d) and scaled by sqrt(d).  Each block of block_rows
+ * (64 or 128) rows gets e, the smallest integer with max|y| <= 448 * 2^e
+ * (0 for an all-zero block), and stores codes e4m3(y * 2^-e).  The
+ * dequantised value is e4m3_value(code) * 2^e.  Rows past N are not read.
+ *
+ * fa2_fwd_fp8 -- attention of quantised q (block_rows 128), k and v
+ * (block_rows 64; v never rotated): o = softmax(s q~ k~^T + mask) v~ with
+ * q~, k~, v~ the dequantised values and s = scale, or scale / d when q and
+ * k were quantised with the same signs (rotated != 0: the two sqrt(d)
+ * factors cancel the transform's scaling, so the scores are those of the
+ * unrotated inputs up to quantisation).  o: bf16 [B][H][N][d]; lse as for
+ * fa2_fwd.  P is rounded to e4m3 for the P.V product (fp32 accumulation).
+ * Same shape, mask, alignment and error rules as fa2_fwd; the exponent
+ * arrays must not overlap the outputs.
+ */
+int fa2_quantize_fp8(const void *x, void *codes, int *exps, int B, int H,
+                     int N, int d, int block_rows, const float *signs,
+                     void *stream);
+int fa2_fwd_fp8(const void *q8, const int *q_exp, const void *k8,
+                const int *k_exp, const void *v8, const int *v_exp, void *o,
+                float *lse, int B, int H, int N, int d, float scale,
+                int rotated, int causal, void *stream);
+/* fa2_fwd_fp8_o32 -- fa2_fwd_fp8 with a float [B][H][N][d] output. */
+int fa2_fwd_fp8_o32(const void *q8, const int *q_exp, const void *k8,
+                    const int *k_exp, const void *v8, const int *v_exp,
+                    float *o, float *lse, int B, int H, int N, int d,
+                    float scale, int rotated, int causal, void *stream);
+
+/*
  * fa2_fwd_fp32 -- float32 q, k, v and o; every step (scores, softmax,
  * probabilities, P.V) in fp32 arithmetic, for exactness checks on small
  * problems.  Same shapes, mask, scale, lse, alignment and error rules.
@@ -209,8 +250,8 @@ int fa2_bwd_o32(const void *q, const void *k, const void *v, const void *o,
 /* Static English description of a return code (never NULL). */
 const char *fa2_strerror(int code);
 
-/* Library ABI version: 4 (2 added the backward pass, 3 grouped K/V heads,
-   4 split key ranges with separate query and key lengths). */
+/* Library ABI version: 5 (2 added the backward pass, 3 grouped K/V heads,
+   4 split key ranges with separate query and key lengths, 5 the FP8 path). */
 int fa2_version(void);
 
 #ifdef __cplusplus

@@ -14,7 +14,11 @@ each step follows, is stated in the C file's header:
 * ``O = P V`` and ``lse = m + ln(sum exp(S - m))`` (natural log);
 * the exact gradients ``dQ, dK, dV`` of that definition for an incoming
   gradient ``dO`` (``dV = P^T dO``, ``dS = P * (dO V^T - D)``,
-  ``dQ = scale dS K``, ``dK = scale dS^T Q``, ``D_i = sum_j P_ij dP_ij``).
+  ``dQ = scale dS K``, ``dK = scale dS^T Q``, ``D_i = sum_j P_ij dP_ij``);
+* FP8 block quantisation with incoherent processing (``quantize_fp8``):
+  a random-sign Walsh-Hadamard rotation, a power-of-two scale per block of
+  rows, e4m3 codes -- the FlashAttention-3 FP8 recipe of the itimpress.au
+  page, section 1.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms,
 invariants, the two-block merge rule from the online-softmax section of the
@@ -278,3 +282,116 @@ def attention_gqa(q, k, v, scale: float, causal: bool = False, nthreads: int = 0
     h = _f64(q).shape[-3]
     return attention(q, expand_kv_heads(k, h), expand_kv_heads(v, h), scale,
                      causal, nthreads)
+
+
+# ---------------------------------------------------------------------------
+# FP8 block quantisation (itimpress.au page "FlashAttention scaling, multi-GPU
+# training and weight quantisation", section 1: small tiles scaled
+# independently; Q and K multiplied by a random orthogonal matrix first).
+
+E4M3_MAX = 448.0
+
+
+def fwht_f32(x):
+    """Unnormalised Walsh-Hadamard transform of the last axis (a power of
+    two), in float32, one butterfly stage at a time for h = 1, 2, 4, ...:
+    (a, b) -> (a + b, a - b) for every pair (i, i + h) inside blocks of 2h.
+    Each output of a stage is one IEEE float32 addition, so any
+    implementation with the same stages gives the same bits.  Applying it
+    twice multiplies by the length."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    d = y.shape[-1]
+    if d & (d - 1):
+        raise ValueError("length must be a power of two")
+    h = 1
+    while h < d:
+        z = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+        a = z[..., 0, :].copy()
+        b = z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(y.shape)
+        h *= 2
+    return y
+
+
+def block_exponent(amax):
+    """Smallest integer e with amax <= 448 * 2^e (0 for amax == 0): the
+    power-of-two scale that maps a block's largest magnitude into the e4m3
+    range."""
+    # amax = m * 2^E with 0.5 <= m < 1 and 448 = 0.875 * 2^9, so
+    # amax <= 448 * 2^e  <=>  m * 2^E <= 0.875 * 2^(9 + e): the smallest such
+    # e is E - 9 when m <= 0.875 and E - 8 otherwise (no rounded division)
+    amax = np.asarray(amax, dtype=np.float64)
+    m, ex = np.frexp(amax)
+    e = np.where(m <= 0.875, ex - 9, ex - 8).astype(np.int32)
+    return np.where(amax > 0, e, 0).astype(np.int32)
+
+
+def to_e4m3_codes(x):
+    """Round float32 values to e4m3 (OCP FP8, round to nearest even) and
+    return the codes as uint8 (torch's float8_e4m3fn conversion)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_values(codes):
+    """The float64 values of e4m3 codes."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def quantize_fp8(x, block_rows: int, signs=None):
+    """Block-quantise ``x`` ``[..., N, d]`` (exact values, e.g. bf16).
+
+    With ``signs`` (``d`` values of +-1) each row is first multiplied by the
+    signs and transformed with :func:`fwht_f32` -- the rotation by the
+    orthogonal matrix diag(signs) H / sqrt(d), with the 1/sqrt(d) left to
+    the caller.  Each block of ``block_rows`` rows (per leading index) gets
+    the exponent e of :func:`block_exponent` for its largest magnitude and
+    stores e4m3(y * 2^-e).  Returns ``(codes uint8 [..., N, d], exps int32
+    [..., ceil(N / block_rows)])``; the dequantised value is
+    ``e4m3_values(codes) * 2^e``."""
+    y = np.asarray(_f64(x), dtype=np.float32)  # exact for bf16 inputs
+    if signs is not None:
+        y = fwht_f32(y * np.asarray(signs, dtype=np.float32))
+    n, d = y.shape[-2], y.shape[-1]
+    nb = -(-n // block_rows)
+    pad = nb * block_rows - n
+    yp = np.concatenate([y, np.zeros(y.shape[:-2] + (pad, d), np.float32)], axis=-2) if pad else y
+    blocks = yp.reshape(yp.shape[:-2] + (nb, block_rows, d))
+    amax = np.abs(blocks).max(axis=(-2, -1))
+    e = block_exponent(amax)
+    scaled = blocks * np.ldexp(np.float32(1), -e)[..., None, None].astype(np.float32)
+    codes = to_e4m3_codes(scaled).reshape(yp.shape)
+    return codes[..., :n, :], e
+
+
+def dequantize_fp8(codes, exps, block_rows: int):
+    """float64 values of block-quantised codes (see :func:`quantize_fp8`)."""
+    v = e4m3_values(codes)
+    n = v.shape[-2]
+    rep = np.repeat(exps, block_rows, axis=-1)[..., :n].astype(np.float64)
+    return v * np.exp2(rep)[..., None]
+
+
+def attention_fp8_reference(q, k, v, scale: float, causal: bool = False,
+                            signs=None, q_rows: int = 128, kv_rows: int = 64):
+    """Exact attention (fp64) of the block-quantised inputs: what an FP8
+    kernel computes before its own roundings (of P and of the output).
+    Q and K are quantised with ``signs`` (rotation) if given, Q in blocks of
+    ``q_rows`` rows, K and V in blocks of ``kv_rows``; the rotation's
+    1/sqrt(d) factors multiply into scale / d.  Returns ``(o, lse, codes)``
+    with ``codes = ((q8, qe), (k8, ke), (v8, ve))``."""
+    d = _f64(q).shape[-1]
+    q8, qe = quantize_fp8(q, q_rows, signs)
+    k8, ke = quantize_fp8(k, kv_rows, signs)
+    v8, ve = quantize_fp8(v, kv_rows, None)
+    qd = dequantize_fp8(q8, qe, q_rows)
+    kd = dequantize_fp8(k8, ke, kv_rows)
+    vd = dequantize_fp8(v8, ve, kv_rows)
+    s_eff = scale / d if signs is not None else scale
+    o, lse, _ = attention(qd, kd, vd, s_eff, causal)
+    return o, lse, ((q8, qe), (k8, ke), (v8, ve))

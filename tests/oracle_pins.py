@@ -342,6 +342,73 @@ def pin_offset_causal(orc):
     assert np.all(o3[:, :4] == 0) and np.all(np.isneginf(l3[:, :4]))
 
 
+def pin_fwht_is_hadamard(orc):
+    """The fast transform equals multiplication by the Sylvester Hadamard
+    matrix (built with Kronecker products) on small integers, where float32
+    is exact; applying it twice gives d times the input."""
+    import oracle as orc_mod
+    r = _rng(40)
+    for d in (8, 64, 128):
+        H = np.array([[1.0]])
+        while H.shape[0] < d:
+            H = np.kron(H, np.array([[1.0, 1.0], [1.0, -1.0]]))
+        x = r.integers(-50, 50, (5, d)).astype(np.float32)
+        y = orc_mod.fwht_f32(x)
+        assert np.array_equal(y.astype(np.float64), x.astype(np.float64) @ H), d
+        assert np.array_equal(orc_mod.fwht_f32(y), x * d), d
+
+
+def pin_e4m3_codes(orc):
+    """e4m3 (OCP FP8: bias 7, 3 mantissa bits, no infinities, max 448) by
+    its definition: the codes of 1, 2, 448, the smallest normal 2^-6 and the
+    smallest subnormal 2^-9; round to nearest even at ties (1 + 1/16 -> 1,
+    1 + 3/16 -> 1 + 1/4); values past 448 but below the next rounding
+    boundary 464 -> 448."""
+    import oracle as orc_mod
+    vals = np.array([1.0, 2.0, 448.0, 2.0 ** -6, 2.0 ** -9, -1.0, 0.0,
+                     1.0625, 1.1875, 450.0, 3.0 * 2.0 ** -9], dtype=np.float32)
+    want = [0x38, 0x40, 0x7E, 0x08, 0x01, 0xB8, 0x00, 0x38, 0x3A, 0x7E, 0x03]
+    assert orc_mod.to_e4m3_codes(vals).tolist() == want
+    assert np.array_equal(orc_mod.e4m3_values(np.array(want, dtype=np.uint8)),
+                          np.array([1, 2, 448, 2.0 ** -6, 2.0 ** -9, -1, 0, 1,
+                                    1.25, 448, 3.0 * 2.0 ** -9]))
+
+
+def pin_block_exponent(orc):
+    """The block scale exponent is the smallest e with amax <= 448 * 2^e."""
+    import oracle as orc_mod
+    a = np.array([448.0, 448.5, 224.0, 224.25, 1.0, 0.875, 0.0, 3.5e-5, 7e4])
+    e = orc_mod.block_exponent(a)
+    assert e.tolist() == [0, 1, -1, 0, -8, -9, 0, -23, 8], e.tolist()
+    for ai, ei in zip(a[a > 0], e[a > 0]):
+        assert ai <= 448 * 2.0 ** ei and ai > 448 * 2.0 ** (ei - 1)
+
+
+def pin_fp8_quantize_error(orc):
+    """Block quantisation error: each dequantised value is within half an
+    e4m3 step of its (rotated) input -- 2^-4 relative for normals, 2^-10
+    times the block scale below them -- and every block uses the top of the
+    e4m3 range; with the rotation, inner products of rows are those of the
+    unrotated rows times d (the transform is d^(1/2) times orthogonal)."""
+    import oracle as orc_mod
+    r = _rng(41)
+    x = r.standard_normal((3, 200, 64)).astype(np.float32)
+    x[:, 7] *= 30.0
+    signs = r.choice([-1.0, 1.0], 64)
+    for sg in (None, signs):
+        c, e = orc_mod.quantize_fp8(x, 64, sg)
+        y = orc_mod.fwht_f32(x * sg) if sg is not None else x
+        dq = orc_mod.dequantize_fp8(c, e, 64)
+        scale = np.exp2(np.repeat(e, 64, axis=-1)[..., :200])[..., None]
+        tol = np.maximum(np.abs(y) * 2.0 ** -4, scale * 2.0 ** -10)
+        assert np.all(np.abs(dq - y) <= tol + 1e-30)
+        amax_codes = np.abs(orc_mod.e4m3_values(c)).reshape(3, -1)
+        assert np.all(amax_codes.max(axis=1) >= 224)
+    yq = orc_mod.fwht_f32(x[0] * signs).astype(np.float64)
+    _close(yq @ yq.T, 64.0 * (x[0].astype(np.float64) @ x[0].T.astype(np.float64)),
+           tol=1e-6, what="rotation inner products")
+
+
 # ---------------------------------------------------------------------------
 # gradients
 
@@ -493,6 +560,10 @@ ALL_PINS = [
     pin_rows_match_full,
     pin_gqa_head_map,
     pin_offset_causal,
+    pin_fwht_is_hadamard,
+    pin_e4m3_codes,
+    pin_block_exponent,
+    pin_fp8_quantize_error,
     pin_bwd_finite_differences,
     pin_bwd_sums,
     pin_bwd_constant_v,

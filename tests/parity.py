@@ -57,6 +57,30 @@ def compare_grad(g, g_ref, heavy=False):
                 ok=finite and rel_l2 <= lim_l2 and max_rel <= lim_max)
 
 
+# FP8 path (fa2_quantize_fp8 + fa2_fwd_fp8).  No tolerance is stated for
+# it; the bounds come from a rounding model (test_fp8_tolerance_model.py):
+# against the exact attention of the dequantised inputs the only roundings
+# left are P in e4m3 (3 mantissa bits) and the output, and the model's
+# error is rel-L2 <= 2.4e-2, max|err|/max|ref| <= 2.1e-2; against the exact
+# attention of the original bf16 inputs (quantisation included) 5.3e-2 on
+# standard normal inputs, and with three outlier channels x20 in Q and K
+# 8.5e-2 when Q and K are rotated (2.7e-1 to 3.5e-1 without the rotation).
+FP8_REL_L2 = 6e-2
+FP8_MAX_REL = 6e-2
+FP8_E2E_REL_L2 = 1.2e-1
+FP8_E2E_ROT_OUTLIER_REL_L2 = 1.5e-1
+
+
+def compare_fp8(o, o_ref):
+    """Error figures of an FP8-path output against a reference."""
+    o = np.asarray(o, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    finite = bool(np.all(np.isfinite(o)))
+    rel_l2 = float(np.linalg.norm(o - o_ref) / max(np.linalg.norm(o_ref), 1e-300))
+    max_rel = float(np.abs(o - o_ref).max() / max(np.abs(o_ref).max(), 1e-300))
+    return dict(finite=finite, rel_l2=rel_l2, max_rel=max_rel)
+
+
 def ulp_bf16(x):
     """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
     ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)

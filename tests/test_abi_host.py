@@ -50,7 +50,7 @@ def test_codes_match_header():
 
 
 def test_version_and_strerror(L):
-    assert fa2.version() == 4
+    assert fa2.version() == 5
     seen = set()
     for name, code in header_codes().items():
         msg = fa2.strerror(code)
@@ -253,3 +253,32 @@ def test_default_splits():
     assert fa2.default_splits(1, 1, 1, 300, 128) == 1
     # already enough workgroups: no split
     assert fa2.default_splits(2, 16, 8192, 8192, 128) == 1
+
+
+def test_fp8_validation(L):
+    Lb = fa2.lib()
+    X, C, E, S = (0x10000000 + i * 64 * MiB for i in range(4))
+    qz = lambda **kw: Lb.fa2_quantize_fp8(*[kw.get(n, v) for n, v in (
+        ("x", X), ("codes", C), ("exps", E))], kw.get("B", 1), kw.get("H", 2),
+        kw.get("N", 100), kw.get("d", 128), kw.get("R", 64), kw.get("signs", S), None)
+    assert qz(x=None) == fa2.FA2_ERR_NULL and qz(exps=None) == fa2.FA2_ERR_NULL
+    assert qz(R=32) == fa2.FA2_ERR_SHAPE and qz(N=0) == fa2.FA2_ERR_SHAPE
+    assert qz(d=96) == fa2.FA2_ERR_HEADDIM
+    assert qz(codes=C + 8) == fa2.FA2_ERR_ALIGN and qz(exps=E + 2) == fa2.FA2_ERR_ALIGN
+    assert qz(codes=X + 64) == fa2.FA2_ERR_ALIAS and qz(exps=C + 64) == fa2.FA2_ERR_ALIAS
+    P = [0x10000000 + i * 64 * MiB for i in range(8)]  # q8 qe k8 ke v8 ve o lse
+    for fn in ("fa2_fwd_fp8", "fa2_fwd_fp8_o32"):
+        f = getattr(Lb, fn)
+        call = lambda ptrs, N=100, d=128, scale=0.1: f(*ptrs, 1, 2, N, d, scale, 1, 1, None)
+        for i in range(7):
+            bad = list(P)
+            bad[i] = None
+            assert call(bad) == fa2.FA2_ERR_NULL, (fn, i)
+        assert call(P, d=32) == fa2.FA2_ERR_HEADDIM
+        assert call(P, scale=float("nan")) == fa2.FA2_ERR_SCALE
+        bad = list(P); bad[1] += 2
+        assert call(bad) == fa2.FA2_ERR_ALIGN
+        bad = list(P); bad[6] = P[1]          # o over q's exponents
+        assert call(bad) == fa2.FA2_ERR_ALIAS
+        bad = list(P); bad[6] = P[0] + 64     # o over q's codes
+        assert call(bad) == fa2.FA2_ERR_ALIAS
