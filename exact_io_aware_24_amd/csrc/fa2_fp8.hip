@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_internal.h"
 
@@ -290,94 +292,131 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Params p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    if (t + 1 < ntiles) {
-      issue_tile8<D>(p.k + head, head_bytes, (t + 1) * kTile * D, kbuf(b ^ 1), wv, false);
-      issue_tile8<D>(p.v + head, head_bytes, (t + 1) * kTile * D, vbuf(b ^ 1), wv, true);
+  // one tile; MASKED (diagonal or ragged tiles) is a compile-time switch so
+  // that the unmasked tiles carry no mask or select instructions
+  // ct_c: this tile's scores -> base-2 logits; shift (<= 0): its V exponent
+  // relative to the head's largest
+  auto tile = [&](auto masked_tag, int t, const char *kb, const char *vb,
+                  float ct_c, float shift) {
+    constexpr bool masked = decltype(masked_tag)::value;
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < C::STEPS; ++st) {
+        const u32x4 lo = lds_load<u32x4>(kb, krd[st][0] + kt * 32 * D);
+        const u32x4 hi = lds_load<u32x4>(kb, krd[st][1] + kt * 32 * D);
+        const i32x8 a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        s[kt] = mfma_fp8(a, qreg[st], s[kt]);
+      }
     }
-    if (t < w_tiles) {
-      const char *kb = kbuf(b), *vb = vbuf(b);
-      const float ct_c = ldexpf(cq, eq + kex[t]);  // scores -> base-2 logits
-      const float shift = static_cast<float>(vex[t] - em);  // <= 0
-      f32x16 s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-        for (int st = 0; st < C::STEPS; ++st) {
-          const u32x4 lo = lds_load<u32x4>(kb, krd[st][0] + kt * 32 * D);
-          const u32x4 hi = lds_load<u32x4>(kb, krd[st][1] + kt * 32 * D);
-          const i32x8 a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          s[kt] = mfma_fp8(a, qreg[st], s[kt]);
-        }
-      }
-      // register r of sub-tile kt holds key 64t + 32kt + 8(r/4) + 4hh + r%4
-      const bool masked = t >= n_full;
-      if (masked) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = t * kTile + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= N || (CAUSAL && key > qi)) s[kt][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      float mlo, mhi;
-      halves(mx, mlo, mhi);
-      mx = fmaxf(mlo, mhi);
-      const float m_tile = mx == -INFINITY ? -INFINITY : mx * ct_c;
-      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int ct = 0; ct < C::NCT; ++ct)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[ct][r] *= alpha;
-      }
-      const float mu = (m_run == -INFINITY ? 0.f : m_run) - shift;
-      float x[2][16];
-      float rs = 0.f;
+    // register r of sub-tile kt holds key 64t + 32kt + 8(r/4) + 4hh + r%4
+    if (masked) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = fast_exp2(__builtin_fmaf(s[kt][r], ct_c, -mu));
-          if (masked) v = s[kt][r] == -INFINITY ? 0.f : v;
-          x[kt][r] = v;
-          rs += v;
+          const int key = t * kTile + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= N || (CAUSAL && key > qi)) s[kt][r] = -INFINITY;
         }
-      l_run += ldexpf(rs, -static_cast<int>(shift));  // P = P' 2^-shift
-      // P' (<= 2^8) as e4m3, key order 32kt + 8a + 4hh + b -> byte 16kt + 4a + b
-      i32x8 pb;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int kt = w >> 2, r0 = 4 * (w & 3);
-        pb[w] = cvt_fp8x4(x[kt][r0], x[kt][r0 + 1], x[kt][r0 + 2], x[kt][r0 + 3]);
-      }
-#pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct) {
-        i32x2 r4[4];
-#pragma unroll
-        for (int rd = 0; rd < 4; ++rd)
-          r4[rd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_i32x2 *)(vb + vrd[ct] + rd * 16 * D));
-        const i32x8 a = i32x8{r4[0][0], r4[0][1], r4[1][0], r4[1][1],
-                              r4[2][0], r4[2][1], r4[3][0], r4[3][1]};
-        oacc[ct] = mfma_fp8(a, pb, oacc[ct]);
-      }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    float mlo, mhi;
+    halves(mx, mlo, mhi);
+    mx = fmaxf(mlo, mhi);
+    const float m_tile = mx == -INFINITY ? -INFINITY : mx * ct_c;
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[ct][r] *= alpha;
+    }
+    const float mu = (m_run == -INFINITY ? 0.f : m_run) - shift;
+    float x[2][16];
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = fast_exp2(__builtin_fmaf(s[kt][r], ct_c, -mu));
+        if (masked) v = s[kt][r] == -INFINITY ? 0.f : v;
+        x[kt][r] = v;
+        rs += v;
+      }
+    l_run += ldexpf(rs, -static_cast<int>(shift));  // P = P' 2^-shift
+    // P' (<= 2^8) as e4m3, key order 32kt + 8a + 4hh + b -> byte 16kt + 4a + b
+    i32x8 pb;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kt = w >> 2, r0 = 4 * (w & 3);
+      pb[w] = cvt_fp8x4(x[kt][r0], x[kt][r0 + 1], x[kt][r0 + 2], x[kt][r0 + 3]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct) {
+      i32x2 r4[4];
+#pragma unroll
+      for (int rd = 0; rd < 4; ++rd)
+        r4[rd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2 *)(vb + vrd[ct] + rd * 16 * D));
+      const i32x8 a = i32x8{r4[0][0], r4[0][1], r4[1][0], r4[1][1],
+                            r4[2][0], r4[2][1], r4[3][0], r4[3][1]};
+      oacc[ct] = mfma_fp8(a, pb, oacc[ct]);
+    }
+  };
+
+  // tile t + 1 into the other buffers, and its exponents (loaded with the
+  // tile so that they have arrived by the barrier that publishes it; a
+  // later load would make the in-order counter wait for the prefetch too)
+  int ek_n = ntiles > 0 ? kex[0] : 0, ev_n = ntiles > 0 ? vex[0] : 0;
+  // the tile constants are formed after the barrier, once the exponents are
+  // known to have arrived
+  auto consts = [&](float &ct_c, float &shift) {
+    ct_c = ldexpf(cq, eq + ek_n);
+    shift = static_cast<float>(ev_n - em);
+  };
+  float ct_c = 0.f, shift = 0.f;
+  auto prefetch = [&](int t) {
+    if (t + 1 < ntiles) {
+      const int nb = (t + 1) & 1;
+      issue_tile8<D>(p.k + head, head_bytes, (t + 1) * kTile * D, kbuf(nb), wv, false);
+      issue_tile8<D>(p.v + head, head_bytes, (t + 1) * kTile * D, vbuf(nb), wv, true);
+      ek_n = kex[t + 1];
+      ev_n = vex[t + 1];
+    }
+  };
+  // unmasked tiles (every wave needs them), then the diagonal / ragged ones
+  // The empty asm uses the exponents right after each barrier: any wait the
+  // compiler adds for them lands there (where the counter is already zero)
+  // and not after the next prefetch, which volatile asm cannot pass.
+  auto arrived = [&]() { asm volatile("" : : "v"(ek_n), "v"(ev_n)); };
+  arrived();
+  int t = 0;
+  for (; t < n_full; ++t) {
+    consts(ct_c, shift);
+    prefetch(t);
+    tile(std::false_type{}, t, kbuf(t & 1), vbuf(t & 1), ct_c, shift);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    arrived();
+  }
+  for (; t < ntiles; ++t) {
+    consts(ct_c, shift);
+    prefetch(t);
+    if (t < w_tiles) tile(std::true_type{}, t, kbuf(t & 1), vbuf(t & 1), ct_c, shift);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    arrived();
   }
 
   float llo, lhi;
