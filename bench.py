@@ -49,7 +49,8 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 CSRC = os.path.join(ROOT, "exact_io_aware_24_amd", "csrc")
 KERNEL_SRCS = {"fwd": ("fa2_fwd_bf16.hip", "fa2_device.h"),
-               "bwd": ("fa2_bwd_bf16.hip", "fa2_device.h")}
+               "bwd": ("fa2_bwd_bf16.hip", "fa2_device.h"),
+               "fp8": ("fa2_fp8.hip", "fa2_device.h")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -84,7 +85,8 @@ def read_traffic(workload_name: str, which: str = "fwd"):
     (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading on
     a copy of known size), or None when there is none or it was taken on a
     different kernel source."""
-    path = os.path.join(PROFILES, "counters_fa2_%s_bf16_%s.md" % (which, workload_name))
+    kind = "fwd_fp8" if which == "fp8" else which + "_bf16"
+    path = os.path.join(PROFILES, "counters_fa2_%s_%s.md" % (kind, workload_name))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -353,8 +355,8 @@ def main(argv=None):
                     "cold_mall_mib": args.cold_mall}
 
     default_entry = "fa2_fwd_splitkv" if decode else "fa2_" + args.which
-    same_shape = not args.seq_len and not args.splits and entry == default_entry
-    traffic = read_traffic(name, args.which) if same_shape else None
+    same_shape = not args.seq_len and not args.splits and entry in (default_entry, "fa2_fwd_fp8")
+    traffic = read_traffic(name, "fp8" if fp8 else args.which) if same_shape else None
     comp = compulsory_bytes(w.B, w.H, w.N, w.d, Nq=w.q_rows, H_kv=w.kv_heads)
     if decode:  # bandwidth-bound: K and V are read once, little arithmetic
         gbs = comp / (ms * 1e-3) / 1e9
@@ -387,7 +389,7 @@ def main(argv=None):
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "score_matrix_bytes_not_written": score_matrix_bytes(w.B, w.H, w.N),
         "compulsory_hbm_bytes": comp,
-        "kernel_source_sha256": kernel_source_hash(args.which),
+        "kernel_source_sha256": kernel_source_hash("fp8" if fp8 else args.which),
         "gpu": torch.cuda.get_device_name(dev),
     }
     if per_call is not None:
