@@ -58,6 +58,15 @@
 //  * Workgroup ids are remapped so that the blocks of one head run on the
 //    same XCD (hardware deals workgroups round-robin over the 8 XCDs), which
 //    keeps that head's K/V in one L2.
+//
+// The same kernel serves the general forward (fa2_fwd_splitkv): Nq queries
+// against Nk keys (causal: query i sits at key position i + Nk - Nq), K/V
+// heads shared by groups of query heads, and the key tiles of a query block
+// split into ranges handled by separate workgroups, each writing fp32
+// partial (O, lse) that merge_splits_kernel combines with the online-softmax
+// merge of the shakilmahmud.com page's section 2.  Tile indices stay global
+// (masks and loads are unchanged); waves whose rows all lie past Nq only
+// help with the loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
