@@ -34,6 +34,7 @@ from __future__ import annotations
 import argparse
 import dataclasses
 import hashlib
+import re
 import json
 import math
 import os
@@ -70,13 +71,21 @@ def compulsory_bytes(B, H, N, d, in_bytes=2, out_bytes=2, lse=True,
     return (nq + 2 * nkv) * in_bytes + nq * out_bytes + (float(B) * H * Nq * 4 if lse else 0)
 
 
+def code_only(text: str) -> str:
+    """Source text without comments, trailing blanks and empty lines, so that
+    an edit of comments alone keeps a counter summary valid."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (ln.split("//", 1)[0].rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash(which: str = "fwd") -> str:
-    """Hash of the kernel sources of one pass (names the kernel version that
-    a counter summary was taken on)."""
+    """Hash of the code (comments excluded) of one pass's kernel sources:
+    names the kernel version that a counter summary was taken on."""
     h = hashlib.sha256()
     for name in KERNEL_SRCS[which]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
