@@ -284,6 +284,32 @@ def attention_gqa(q, k, v, scale: float, causal: bool = False, nthreads: int = 0
                      causal, nthreads)
 
 
+def sum_kv_groups(x, heads_kv: int):
+    """Inverse of :func:`expand_kv_heads` for gradients: ``x`` ``[..., H, N,
+    d]`` summed over each group of H / H_kv consecutive query heads into
+    ``[..., H_kv, N, d]`` (a K/V head used by several query heads receives
+    the sum of their gradients)."""
+    x = _f64(x)
+    h = x.shape[-3]
+    if h % heads_kv != 0:
+        raise ValueError("H_kv = %d does not divide H = %d" % (heads_kv, h))
+    shape = x.shape[:-3] + (heads_kv, h // heads_kv) + x.shape[-2:]
+    return x.reshape(shape).sum(axis=-3)
+
+
+def attention_bwd_gqa(q, k, v, dout, scale: float, causal: bool = False,
+                      nthreads: int = 0):
+    """Gradients of the grouped-head attention (:func:`attention_gqa`):
+    the plain backward on the expanded K/V, then dK, dV summed over each
+    group.  Returns ``(dq, dk, dv, delta, threads_used)`` with dk, dv of
+    shape ``[..., H_kv, N, d]``."""
+    h = _f64(q).shape[-3]
+    hk = _f64(k).shape[-3]
+    dq, dk, dv, delta, used = attention_bwd(q, expand_kv_heads(k, h),
+                                            expand_kv_heads(v, h), dout, scale,
+                                            causal, nthreads)
+    return dq, sum_kv_groups(dk, hk), sum_kv_groups(dv, hk), delta, used
+
 # ---------------------------------------------------------------------------
 # FP8 block quantisation (itimpress.au page "FlashAttention scaling, multi-GPU
 # training and weight quantisation", section 1: small tiles scaled

@@ -449,6 +449,41 @@ def pin_bwd_finite_differences(orc):
                    % (name, (nh, nq, nk, d, scale, causal)))
 
 
+def pin_gqa_bwd_finite_differences(orc):
+    """Grouped K/V heads: every entry of dQ, dK, dV matches the central
+    difference of the grouped forward's loss sum(O * dO), so the shared K/V
+    gradients carry the contributions of exactly the query heads that read
+    them (grouped-query and multi-query cases, causal and not)."""
+    import oracle as orc_mod
+    r = _rng(22)
+    h = 1e-5
+    for B, H, Hk, n, d, scale, causal in ((1, 4, 2, 4, 3, 0.7, True),
+                                          (2, 3, 1, 3, 2, -0.9, False),
+                                          (1, 6, 3, 3, 2, 1.1, True)):
+        q = r.standard_normal((B, H, n, d))
+        k = r.standard_normal((B, Hk, n, d))
+        v = r.standard_normal((B, Hk, n, d))
+        g = r.standard_normal((B, H, n, d))
+        dq, dk, dv, _, _ = orc_mod.attention_bwd_gqa(q, k, v, g, scale, causal)
+
+        def loss():
+            o, _, _ = orc_mod.attention_gqa(q, k, v, scale, causal)
+            return float(np.sum(o * g))
+
+        for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.empty_like(x)
+            for idx in np.ndindex(x.shape):
+                x0 = x[idx]
+                x[idx] = x0 + h
+                lp = loss()
+                x[idx] = x0 - h
+                lm = loss()
+                x[idx] = x0
+                num[idx] = (lp - lm) / (2 * h)
+            _close(grad, num, tol=1e-7, what="gqa d%s finite differences %s"
+                   % (name, (B, H, Hk, n, d, scale, causal)))
+
+
 def pin_bwd_sums(orc):
     """Rows of P sum to one, so sum_j dV_j = sum_i dO_i; the softmax is
     unchanged by a common shift of a row's logits, so sum_j dS_ij = 0 and
@@ -565,6 +600,7 @@ ALL_PINS = [
     pin_block_exponent,
     pin_fp8_quantize_error,
     pin_bwd_finite_differences,
+    pin_gqa_bwd_finite_differences,
     pin_bwd_sums,
     pin_bwd_constant_v,
     pin_bwd_zero_scale,

@@ -59,6 +59,24 @@ def test_gqa_pin_rejects_an_interleaved_head_map(orc, monkeypatch):
         pin_gqa_head_map(orc)
 
 
+def test_gqa_bwd_pin_rejects_interleaved_group_sums(orc, monkeypatch):
+    """A plausible mistake in the gradient of shared K/V heads -- summing
+    query heads h, h + H_kv, ... (an interleaved group) instead of the
+    consecutive group h // (H / H_kv) -- fails the finite-difference pin."""
+    import oracle as orc_mod
+    from oracle_pins import pin_gqa_bwd_finite_differences
+
+    def interleaved(x, heads_kv):
+        x = np.asarray(x, dtype=np.float64)
+        h = x.shape[-3]
+        shape = x.shape[:-3] + (h // heads_kv, heads_kv) + x.shape[-2:]
+        return x.reshape(shape).sum(axis=-4)
+
+    monkeypatch.setattr(orc_mod, "sum_kv_groups", interleaved)
+    with pytest.raises(AssertionError):
+        pin_gqa_bwd_finite_differences(orc)
+
+
 def test_merge_reading_o2_unnormalised(orc):
     """The online-softmax section's O update weights the new block by
     e^(m2-m)/l without an l2 factor; that is only consistent if the new
