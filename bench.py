@@ -9,7 +9,8 @@ headline workload B=2, H=16, N=8192, d=128, causal, inputs resident in HBM
 ``--seq-len`` pick another shape).  ``--pass bwd`` times ``fa2_bwd`` instead
 (gradients for a seeded dO, after one forward call that provides O and lse),
 counted at the usual 2.5x the forward's flop: the five products S, dP, dV,
-dK, dQ.  Workloads with fewer query rows than keys (decoding) run through
+dK, dQ; with shared K/V heads it times ``fa2_bwd_gqa`` (``--gsplits`` sets
+the query-head ranges per K/V head).  Workloads with fewer query rows than keys (decoding) run through
 ``fa2_fwd_splitkv`` with its default key-range split and are reported
 against the HBM roofline (their bytes: K, V, Q read, O and lse written).
 ``--entry fa2_fwd_fp8`` times the FP8 attention on inputs quantised (with
@@ -119,13 +120,15 @@ def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
     workload, as many as fit the budget after timing the first one."""
     import oracle
     BH = w.B * w.H
-    qf, kf, vf, gf = (t.reshape(BH, w.N, w.d) for t in (q, k, v, do))
+    G = w.H // w.kv_heads  # query heads per K/V head
+    qf, gf = (t.reshape(BH, w.N, w.d) for t in (q, do))
+    kf, vf = (t.reshape(BH // G, w.N, w.d) for t in (k, v))
     n_heads, dt, threads = 0, 0.0, 0
     t0 = time.perf_counter()
     while n_heads < BH and (n_heads == 0 or dt * (n_heads + 1) / n_heads <= budget_s):
         h = n_heads
-        _, _, _, _, threads = oracle.attention_bwd(qf[h], kf[h], vf[h], gf[h],
-                                                   w.scale, w.causal)
+        _, _, _, _, threads = oracle.attention_bwd(qf[h], kf[h // G], vf[h // G],
+                                                   gf[h], w.scale, w.causal)
         n_heads += 1
         dt = time.perf_counter() - t0
     flops = 2.5 * w.flops / BH * n_heads
@@ -207,6 +210,9 @@ def main(argv=None):
                     help="override the workload's sequence length")
     ap.add_argument("--splits", type=int, default=0,
                     help="key ranges for fa2_fwd_splitkv workloads (0: the default)")
+    ap.add_argument("--gsplits", type=int, default=0,
+                    help="query-head ranges per shared K/V head for the grouped "
+                         "backward (0: the default)")
     ap.add_argument("--per-call", action="store_true",
                     help="also time single calls (median, min)")
     ap.add_argument("--cold-mall", type=int, default=0, metavar="MIB",
@@ -247,9 +253,6 @@ def main(argv=None):
               file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
-    if args.which == "bwd" and w.kv_heads != w.H:
-        print("the backward pass takes one K/V head per query head", file=sys.stderr)
-        return 2
     decode = w.q_rows != w.N
     if entry == "fa2_fwd_fp8" and (decode or w.kv_heads != w.H):
         print("fa2_fwd_fp8 takes equal query and key lengths and one K/V head per "
@@ -265,6 +268,7 @@ def main(argv=None):
     out_dtype = torch.float32 if entry.endswith("_o32") else torch.bfloat16
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
     n_splits = None
+    n_gsplits = None
     fp8 = entry == "fa2_fwd_fp8"
     quant_ms = None
     if fp8:
@@ -315,13 +319,21 @@ def main(argv=None):
         do = wl.make_dout(w.B, w.H, w.N, w.d)
         dod = do.to(dev)
         o, _ = fa2.forward(qd, kd, vd, causal=w.causal, scale=w.scale, lse=lse)
-        grads = [torch.empty(qd.shape, dtype=out_dtype, device=dev) for _ in range(3)]
+        grads = [torch.empty(t.shape, dtype=out_dtype, device=dev) for t in (qd, kd, vd)]
         delta = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        dkv_part = None
+        if w.kv_heads != w.H:  # shared K/V heads: the grouped entry point
+            entry = entry.replace("fa2_bwd", "fa2_bwd_gqa")
+            n_gsplits = args.gsplits or fa2.default_gsplits(w.B, w.H, w.kv_heads, w.N)
+            if n_gsplits > 1:
+                dkv_part = torch.empty((2, n_gsplits) + tuple(kd.shape),
+                                       dtype=torch.float32, device=dev)
 
         def step():
             fa2.backward(qd, kd, vd, o, dod, lse, causal=w.causal, scale=w.scale,
                          out_dtype=out_dtype, dq=grads[0], dk=grads[1],
-                         dv=grads[2], delta=delta)
+                         dv=grads[2], delta=delta, n_gsplits=n_gsplits,
+                         dkv_part=dkv_part)
 
     for _ in range(args.warmup):
         step()
@@ -364,7 +376,8 @@ def main(argv=None):
                     "cold_mall_mib": args.cold_mall}
 
     default_entry = "fa2_fwd_splitkv" if decode else "fa2_" + args.which
-    same_shape = not args.seq_len and not args.splits and entry in (default_entry, "fa2_fwd_fp8")
+    same_shape = not args.seq_len and not args.splits and not args.gsplits and \
+        entry in (default_entry, "fa2_fwd_fp8", "fa2_bwd_gqa")
     traffic = read_traffic(name, "fp8" if fp8 else args.which) if same_shape else None
     comp = compulsory_bytes(w.B, w.H, w.N, w.d, Nq=w.q_rows, H_kv=w.kv_heads)
     if decode:  # bandwidth-bound: K and V are read once, little arithmetic
@@ -393,7 +406,7 @@ def main(argv=None):
         "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.kv_heads,
                    "Nq": w.q_rows, "N": w.N, "d": w.d, "causal": w.causal,
                    "scale": w.scale, "flops_per_step": flops, "entry_point": entry,
-                   "n_splits": n_splits},
+                   "n_splits": n_splits, "n_gsplits": n_gsplits},
         "roofline": roofline,
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "score_matrix_bytes_not_written": score_matrix_bytes(w.B, w.H, w.N),

@@ -33,7 +33,8 @@ FA2_ERR_HIP = -7
 EXPORTED = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_gqa", "fa2_fwd_gqa_o32",
             "fa2_fwd_splitkv", "fa2_fwd_splitkv_o32", "fa2_quantize_fp8",
             "fa2_fwd_fp8", "fa2_fwd_fp8_o32", "fa2_fwd_fp32", "fa2_bwd",
-            "fa2_bwd_o32", "fa2_strerror", "fa2_version")
+            "fa2_bwd_o32", "fa2_bwd_gqa", "fa2_bwd_gqa_o32", "fa2_strerror",
+            "fa2_version")
 MAX_SPLITS = 1024  # FA2_MAX_SPLITS
 
 _lock = threading.Lock()
@@ -85,6 +86,11 @@ def lib() -> ctypes.CDLL:
         for name in ("fa2_bwd", "fa2_bwd_o32"):
             f = getattr(L, name)
             f.argtypes = bsig
+            f.restype = ctypes.c_int
+        gbsig = [vp] * 10 + [i] * 5 + [ctypes.c_float, i, i, vp, vp]
+        for name in ("fa2_bwd_gqa", "fa2_bwd_gqa_o32"):
+            f = getattr(L, name)
+            f.argtypes = gbsig
             f.restype = ctypes.c_int
         L.fa2_strerror.argtypes = [i]
         L.fa2_strerror.restype = ctypes.c_char_p
@@ -202,34 +208,49 @@ def raw_call(fn: str, q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, scale,
                                   d, ctypes.c_float(scale), int(causal), stream))
 
 
+def default_gsplits(B: int, H: int, H_kv: int, N: int) -> int:
+    """A count of query-head ranges per shared K/V head for the grouped
+    backward that gives the dK/dV kernel about 1024 workgroups (two per
+    compute unit, twice over), at most one range per query head."""
+    units = B * H_kv * ((N + 127) // 128)
+    return int(max(1, min(H // H_kv, -(-1024 // units))))
+
+
 def backward(q, k, v, o, dout, lse, causal: bool = False,
              scale: float | None = None, out_dtype=None, dq=None, dk=None,
-             dv=None, delta=None):
+             dv=None, delta=None, n_gsplits: int | None = None, dkv_part=None):
     """Gradients of :func:`forward` with respect to ``q, k, v``.
 
-    ``q, k, v, o, dout``: contiguous bfloat16 GPU tensors ``[B, H, N, d]``
-    (the forward's inputs and output, and the gradient of the loss with
-    respect to ``o``); ``lse``: the forward's float32 ``[B, H, N]``.
-    ``causal`` and ``scale`` must be the forward's.  ``out_dtype``:
-    ``torch.bfloat16`` (default, ``fa2_bwd``) or ``torch.float32``
-    (``fa2_bwd_o32``).  ``dq, dk, dv`` and the float32 ``[B, H, N]``
-    workspace ``delta`` may be preallocated.  Returns ``(dq, dk, dv)``.
-    The kernels are enqueued on torch's current stream.
+    ``q, o, dout``: contiguous bfloat16 GPU tensors ``[B, H, N, d]`` (the
+    forward's query input and output, and the gradient of the loss with
+    respect to ``o``); ``k, v``: ``[B, H, N, d]`` or, with key/value heads
+    shared by groups of query heads, ``[B, H_kv, N, d]``; ``lse``: the
+    forward's float32 ``[B, H, N]``.  ``causal`` and ``scale`` must be the
+    forward's.  ``out_dtype``: ``torch.bfloat16`` (default, ``fa2_bwd``) or
+    ``torch.float32`` (``fa2_bwd_o32``); grouped K/V heads call
+    ``fa2_bwd_gqa[_o32]`` with ``n_gsplits`` query-head ranges per K/V head
+    (default :func:`default_gsplits`) and the float32 workspace
+    ``dkv_part`` ``[2, n_gsplits, B, H_kv, N, d]`` (allocated when needed
+    and not given).  ``dq, dk, dv`` and the float32 ``[B, H, N]`` workspace
+    ``delta`` may be preallocated.  Returns ``(dq, dk, dv)``.  The kernels
+    are enqueued on torch's current stream.
     """
     import torch
-    _check_tensors(q, k, v)
+    _check_tensors(q, k, v, grouped=True)
     _check_tensors(o, dout, q)
     if q.dtype != torch.bfloat16 or o.dtype != torch.bfloat16 \
             or dout.dtype != torch.bfloat16:
         raise ValueError("q, k, v, o and dout must be bfloat16")
     B, H, N, d = (int(x) for x in q.shape)
+    Hk = int(k.shape[1])
+    grouped = Hk != H or n_gsplits is not None
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     odt = torch.bfloat16 if out_dtype is None else out_dtype
     if odt == torch.bfloat16:
-        fn = "fa2_bwd"
+        fn = "fa2_bwd_gqa" if grouped else "fa2_bwd"
     elif odt == torch.float32:
-        fn = "fa2_bwd_o32"
+        fn = "fa2_bwd_gqa_o32" if grouped else "fa2_bwd_o32"
     else:
         raise ValueError("out_dtype must be bfloat16 or float32")
 
@@ -241,27 +262,42 @@ def backward(q, k, v, o, dout, lse, causal: bool = False,
             raise ValueError("%s must be a contiguous float32 [B, H, N] tensor" % name)
         return t
 
-    def grad(t, name):
+    def grad(t, name, like):
         if t is None:
-            return torch.empty((B, H, N, d), dtype=odt, device=q.device)
-        if t.shape != q.shape or t.dtype != odt or not t.is_contiguous() \
+            return torch.empty(like.shape, dtype=odt, device=q.device)
+        if t.shape != like.shape or t.dtype != odt or not t.is_contiguous() \
                 or t.device != q.device:
-            raise ValueError("%s must be a contiguous %s tensor shaped like q"
-                             % (name, odt))
+            raise ValueError("%s must be a contiguous %s tensor of shape %s"
+                             % (name, odt, tuple(like.shape)))
         return t
 
     if lse is None:
         raise ValueError("lse (from the forward pass) is required")
     lse = vec(lse, "lse")
     delta = vec(delta, "delta")
-    dq, dk, dv = grad(dq, "dq"), grad(dk, "dk"), grad(dv, "dv")
+    dq, dk, dv = grad(dq, "dq", q), grad(dk, "dk", k), grad(dv, "dv", v)
+    if grouped:
+        ns = default_gsplits(B, H, Hk, N) if n_gsplits is None else int(n_gsplits)
+        if ns > 1 and dkv_part is None:
+            dkv_part = torch.empty((2, ns, B, Hk, N, d), dtype=torch.float32,
+                                   device=q.device)
+        if ns > 1 and (dkv_part.dtype != torch.float32 or not dkv_part.is_contiguous()
+                       or dkv_part.numel() < 2 * ns * B * Hk * N * d
+                       or dkv_part.device != q.device):
+            raise ValueError("dkv_part must be a contiguous float32 tensor of at "
+                             "least 2 * n_gsplits * B * H_kv * N * d elements")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = getattr(lib(), fn)(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-            dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(),
-            dk.data_ptr(), dv.data_ptr(), B, H, N, d, ctypes.c_float(scale),
-            int(bool(causal)), stream)
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(),
+                dk.data_ptr(), dv.data_ptr())
+        if grouped:
+            rc = getattr(lib(), fn)(
+                *ptrs, B, H, Hk, N, d, ctypes.c_float(scale), int(bool(causal)),
+                ns, dkv_part.data_ptr() if ns > 1 else None, stream)
+        else:
+            rc = getattr(lib(), fn)(*ptrs, B, H, N, d, ctypes.c_float(scale),
+                                    int(bool(causal)), stream)
     if rc != FA2_OK:
         raise FA2Error(rc, fn)
     return dq, dk, dv
@@ -424,3 +460,13 @@ def raw_call_bwd(fn: str, ptrs, B, H, N, d, scale, causal, stream=None) -> int:
         raise ValueError("ten pointers expected")
     return int(getattr(lib(), fn)(*ptrs, B, H, N, d, ctypes.c_float(scale),
                                   int(causal), stream))
+
+
+def raw_call_bwd_gqa(fn: str, ptrs, B, H, H_kv, N, d, scale, causal, n_gsplits,
+                     dkv_part, stream=None) -> int:
+    """Call a grouped backward entry point with ten raw integer pointers (as
+    :func:`raw_call_bwd`) and the raw workspace pointer; returns the code."""
+    if len(ptrs) != 10:
+        raise ValueError("ten pointers expected")
+    return int(getattr(lib(), fn)(*ptrs, B, H, H_kv, N, d, ctypes.c_float(scale),
+                                  int(causal), n_gsplits, dkv_part, stream))

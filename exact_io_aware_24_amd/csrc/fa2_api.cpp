@@ -91,33 +91,41 @@ fa2::FwdArgs make_args(const void *q, const void *k, const void *v, void *o,
   return a;
 }
 
-// Validation of the backward entry points: every pointer is required; the
-// four outputs (dq, dk, dv and the delta workspace) may overlap neither an
+// Validation of the backward entry points: every pointer is required (the
+// partial-sum workspace only when n_gsplits > 1); the outputs (dq, dk, dv,
+// the delta workspace and the partial-sum workspace) may overlap neither an
 // input nor each other.
 int validate_bwd(const void *q, const void *k, const void *v, const void *o,
                  const void *dout, const float *lse, const float *delta,
                  const void *dq, const void *dk, const void *dv, int B, int H,
-                 int N, int d, float scale, int out_bytes) {
+                 int H_kv, int N, int d, float scale, int out_bytes,
+                 int n_gsplits, const float *dkv_part) {
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv)
     return FA2_ERR_NULL;
   // shape, head dimension, size limits and scale as for the forward
-  int rc = validate(q, k, v, o, nullptr, B, H, H, N, N, d, scale, 2, 2,
+  int rc = validate(q, k, v, o, nullptr, B, H, H_kv, N, N, d, scale, 2, 2,
                     fa2::kBf16BwdRowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc != FA2_OK && rc != FA2_ERR_ALIAS) return rc;
+  if (n_gsplits < 1 || n_gsplits > H / H_kv) return FA2_ERR_SHAPE;
+  if (n_gsplits > 1 && !dkv_part) return FA2_ERR_NULL;
   if (misaligned(dout) || misaligned(lse) || misaligned(delta) ||
-      misaligned(dq) || misaligned(dk) || misaligned(dv))
+      misaligned(dq) || misaligned(dk) || misaligned(dv) ||
+      (n_gsplits > 1 && misaligned(dkv_part)))
     return FA2_ERR_ALIGN;
   const int64_t elems = static_cast<int64_t>(B) * H * N * d;
+  const int64_t kv_elems = static_cast<int64_t>(B) * H_kv * N * d;
   const int64_t rows = static_cast<int64_t>(B) * H * N;
-  const Range in[6] = {span(q, elems * 2),    span(k, elems * 2),
-                       span(v, elems * 2),    span(o, elems * 2),
+  const Range in[6] = {span(q, elems * 2),    span(k, kv_elems * 2),
+                       span(v, kv_elems * 2), span(o, elems * 2),
                        span(dout, elems * 2), span(lse, rows * 4)};
-  const Range out[4] = {span(dq, elems * out_bytes), span(dk, elems * out_bytes),
-                        span(dv, elems * out_bytes), span(delta, rows * 4)};
-  for (int i = 0; i < 4; ++i) {
+  const Range out[5] = {
+      span(dq, elems * out_bytes), span(dk, kv_elems * out_bytes),
+      span(dv, kv_elems * out_bytes), span(delta, rows * 4),
+      span(dkv_part, n_gsplits > 1 ? 2 * n_gsplits * kv_elems * 4 : 0)};
+  for (int i = 0; i < 5; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(out[i], in[j])) return FA2_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = i + 1; j < 5; ++j)
       if (overlaps(out[i], out[j])) return FA2_ERR_ALIAS;
   }
   return FA2_OK;
@@ -126,7 +134,8 @@ int validate_bwd(const void *q, const void *k, const void *v, const void *o,
 fa2::BwdArgs make_bwd_args(const void *q, const void *k, const void *v,
                            const void *o, const void *dout, const float *lse,
                            float *delta, void *dq, void *dk, void *dv, int B,
-                           int H, int N, int d, float scale, int causal) {
+                           int H, int H_kv, int N, int d, float scale,
+                           int causal, int n_gsplits, float *dkv_part) {
   fa2::BwdArgs a;
   a.q = q;
   a.k = k;
@@ -139,6 +148,10 @@ fa2::BwdArgs make_bwd_args(const void *q, const void *k, const void *v,
   a.dk = dk;
   a.dv = dv;
   a.bh = B * H;
+  a.h = H;
+  a.group = H / H_kv;
+  a.n_gsplits = n_gsplits;
+  a.dkv_part = n_gsplits > 1 ? dkv_part : nullptr;
   a.n = N;
   a.d = d;
   a.scale = scale;
@@ -346,17 +359,26 @@ FA2_EXPORT int fa2_fwd_fp32(const float *q, const float *k, const float *v,
       static_cast<hipStream_t>(stream)));
 }
 
+static int bwd(const void *q, const void *k, const void *v, const void *o,
+               const void *dout, const float *lse, float *delta, void *dq,
+               void *dk, void *dv, int B, int H, int H_kv, int N, int d,
+               float scale, int causal, int n_gsplits, float *dkv_part,
+               bool o32, void *stream) {
+  int rc = validate_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv,
+                        N, d, scale, o32 ? 4 : 2, n_gsplits, dkv_part);
+  if (rc != FA2_OK) return rc;
+  return finish(fa2::launch_bwd_bf16(
+      make_bwd_args(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d,
+                    scale, causal, n_gsplits, dkv_part),
+      o32, static_cast<hipStream_t>(stream)));
+}
+
 FA2_EXPORT int fa2_bwd(const void *q, const void *k, const void *v,
                        const void *o, const void *dout, const float *lse,
                        float *delta, void *dq, void *dk, void *dv, int B, int H,
                        int N, int d, float scale, int causal, void *stream) {
-  int rc = validate_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d,
-                        scale, 2);
-  if (rc != FA2_OK) return rc;
-  return finish(fa2::launch_bwd_bf16(
-      make_bwd_args(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale,
-                    causal),
-      false, static_cast<hipStream_t>(stream)));
+  return bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H, N, d, scale,
+             causal, 1, nullptr, false, stream);
 }
 
 FA2_EXPORT int fa2_bwd_o32(const void *q, const void *k, const void *v,
@@ -364,13 +386,28 @@ FA2_EXPORT int fa2_bwd_o32(const void *q, const void *k, const void *v,
                            float *delta, float *dq, float *dk, float *dv, int B,
                            int H, int N, int d, float scale, int causal,
                            void *stream) {
-  int rc = validate_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d,
-                        scale, 4);
-  if (rc != FA2_OK) return rc;
-  return finish(fa2::launch_bwd_bf16(
-      make_bwd_args(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, scale,
-                    causal),
-      true, static_cast<hipStream_t>(stream)));
+  return bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H, N, d, scale,
+             causal, 1, nullptr, true, stream);
+}
+
+FA2_EXPORT int fa2_bwd_gqa(const void *q, const void *k, const void *v,
+                           const void *o, const void *dout, const float *lse,
+                           float *delta, void *dq, void *dk, void *dv, int B,
+                           int H, int H_kv, int N, int d, float scale,
+                           int causal, int n_gsplits, float *dkv_part,
+                           void *stream) {
+  return bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale,
+             causal, n_gsplits, dkv_part, false, stream);
+}
+
+FA2_EXPORT int fa2_bwd_gqa_o32(const void *q, const void *k, const void *v,
+                               const void *o, const void *dout,
+                               const float *lse, float *delta, float *dq,
+                               float *dk, float *dv, int B, int H, int H_kv,
+                               int N, int d, float scale, int causal,
+                               int n_gsplits, float *dkv_part, void *stream) {
+  return bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, scale,
+             causal, n_gsplits, dkv_part, true, stream);
 }
 
 FA2_EXPORT const char *fa2_strerror(int code) {
@@ -389,4 +426,4 @@ FA2_EXPORT const char *fa2_strerror(int code) {
   }
 }
 
-FA2_EXPORT int fa2_version(void) { return 5; }
+FA2_EXPORT int fa2_version(void) { return 6; }

@@ -27,6 +27,14 @@
 // Splitting dQ from dK/dV recomputes S and dP once more but needs neither
 // atomics nor a dQ accumulation buffer.
 //
+// Grouped K/V heads (query head h reads K/V head h / (H / H_kv)): dQ needs
+// only that index map; dK and dV of a shared head are sums over its group of
+// query heads.  A dkdv_kernel workgroup streams the query tiles of every
+// head of one range of the group in turn, accumulating in the same
+// registers; with one range per group it writes dK/dV directly, with several
+// each range writes an fp32 partial and reduce_parts_kernel adds the
+// partials in range order (deterministic, no atomics).
+//
 // MFMA layouts (v_mfma_f32_32x32x16_bf16): A lane l holds A[l%32][8(l/32)
 // .. +7], B lane l holds B[8(l/32) .. +7][l%32], the result register r of
 // lane l is D[8(r/4) + 4(l/32) + r%4][l%32].  Each kernel computes its
@@ -43,6 +51,8 @@
 // stored once and read both ways.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "fa2_device.h"
 #include "fa2_internal.h"
@@ -61,12 +71,23 @@ struct BwdParams {
   const float *lse;
   float *delta;
   void *dq, *dk, *dv;
-  int n;         // sequence length
-  int n_blocks;  // ceil(n / 128)
-  int total;     // bh * n_blocks (grid size)
-  float c;       // scale * log2(e)
+  float *dk_part, *dv_part;  // [n_gsplits][B*H_kv][N][d] (n_gsplits > 1)
+  size_t part_stride;        // B*H_kv*N*d
+  int n;          // sequence length
+  int n_blocks;   // ceil(n / 128)
+  int total;      // B*H*n_blocks (dq grid size)
+  int total_kv;   // B*H_kv*n_gsplits*n_blocks (dkdv grid size)
+  int h;          // query heads per batch index
+  int group;      // query heads per K/V head
+  int n_gsplits;  // ranges of a group's query heads
+  float c;        // scale * log2(e)
   float scale;
 };
+
+// K/V head read by query head bh (both counted over B*H / B*H_kv).
+__device__ __forceinline__ int kv_head(int bh, int h, int group) {
+  return group == 1 ? bh : (bh / h) * (h / group) + (bh % h) / group;
+}
 
 template <int D>
 struct BCfg {
@@ -241,9 +262,11 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t *o,
 
 // ---- dK, dV -----------------------------------------------------------------
 //
-// Workgroup: 128 keys of one head, wave w owns keys k0 + 32w + lane%32.
-// K and V of those keys are B operands held in registers; for each tile of
-// 64 queries (two 32-query halves):
+// Workgroup: 128 keys of one K/V head, wave w owns keys k0 + 32w + lane%32,
+// and one range of the query heads that read this K/V head (all of them, or
+// one of n_gsplits ranges).  K and V of those keys are B operands held in
+// registers; for each query head of the range and each of its tiles of 64
+// queries (two 32-query halves):
 //   S  = Q K^T      A = Q rows (LDS),  B = K (registers)  -> lane = key
 //   dP = dO V^T     A = dO rows (LDS), B = V (registers)
 //   P = exp2(S c - lse log2 e), dS = P (dP - D)
@@ -268,11 +291,17 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
 
-  const int logical = xcd_remap(blockIdx.x, p.total);
-  const int bh = logical / p.n_blocks;
-  const int kb = logical - bh * p.n_blocks;  // causal: block 0 is heaviest
+  const int logical = xcd_remap(blockIdx.x, p.total_kv);
+  const int unit = logical / p.n_blocks;        // (K/V head, query-head range)
+  const int kb = logical - unit * p.n_blocks;   // causal: block 0 is heaviest
+  const int kvbh = unit / p.n_gsplits;
+  const int gs = unit - kvbh * p.n_gsplits;
+  const int hkv = p.h / p.group;
+  const int g_lo = gs * p.group / p.n_gsplits;
+  const int ng = (gs + 1) * p.group / p.n_gsplits - g_lo;  // >= 1
+  const int qbh0 = (kvbh / hkv) * p.h + (kvbh % hkv) * p.group + g_lo;
   const int N = p.n;
-  const size_t head = static_cast<size_t>(bh) * N * D;
+  const size_t head = static_cast<size_t>(kvbh) * N * D;
   const int head_bytes = N * D * 2;
   const int k0 = kb * kBlk;
   const int kw = k0 + 32 * wv;
@@ -287,9 +316,6 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[ct][r] = dv[ct][r] = 0.f;
 
-  const uint16_t *qh = p.q + head, *oh = p.dout + head;
-  const float *lh = p.lse + static_cast<size_t>(bh) * N;
-  const float *dh = p.delta + static_cast<size_t>(bh) * N;
   const TileOffsets<D> off = tile_offsets<D>(lane, wv);
   // statistics: wave 0 loads lse, wave 1 loads D; lanes 16.. read past the
   // end of the buffer (zero) into the unused part of the staging area
@@ -301,13 +327,17 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
   // tiles below this one contain a query before one of the block's keys
   const int t_full = CAUSAL ? (k0 + kBlk - 1 + kTileRows - 1) / kTileRows : 0;
 
-  auto issue = [&](int t, int buf) {
-    issue_tile<D>(qh, head_bytes, off, qbuf(buf), wv, t * kTileRows);
-    issue_tile<D>(oh, head_bytes, off, obuf(buf), wv, t * kTileRows);
+  // tile t of query head qbh0 + g
+  auto issue = [&](int g, int t, int buf) {
+    const size_t rows = static_cast<size_t>(qbh0 + g) * N;
+    issue_tile<D>(p.q + rows * D, head_bytes, off, qbuf(buf), wv, t * kTileRows);
+    issue_tile<D>(p.dout + rows * D, head_bytes, off, obuf(buf), wv, t * kTileRows);
     if (wv == 0)
-      dma16(tile_desc(lh, N * 4, t * kTileRows * 4), st_off, 0, lds_addr(lbuf(buf)));
+      dma16(tile_desc(p.lse + rows, N * 4, t * kTileRows * 4), st_off, 0,
+            lds_addr(lbuf(buf)));
     if (wv == 1)
-      dma16(tile_desc(dh, N * 4, t * kTileRows * 4), st_off, 0, lds_addr(dbuf(buf)));
+      dma16(tile_desc(p.delta + rows, N * 4, t * kTileRows * 4), st_off, 0,
+            lds_addr(dbuf(buf)));
   };
 
   if (N % kTileRows != 0) {  // ragged end: never expose stale LDS bits
@@ -315,14 +345,17 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
       reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
   }
-  if (t0 < nt) issue(t0, 0);
+  if (t0 < nt) issue(0, t0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   const float c = p.c;
-  for (int t = t0; t < nt; ++t) {
-    const int b = (t - t0) & 1;
-    if (t + 1 < nt) issue(t + 1, b ^ 1);
+  // (head, tile) pairs head-major; the next pair's tile is prefetched
+  int b = 0;
+  for (int g = 0; g < ng; ++g)
+  for (int t = t0; t < nt; ++t, b ^= 1) {
+    if (t + 1 < nt) issue(g, t + 1, b ^ 1);
+    else if (g + 1 < ng) issue(g + 1, t0, b ^ 1);
     // this wave's keys all come after every query of the tile: nothing to do
     const bool skip = CAUSAL && (t * kTileRows + kTileRows - 1 < kw);
     if (!skip) {
@@ -370,8 +403,41 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
 
   if (kj < N) {
     const size_t row = head + static_cast<size_t>(kj) * D;
-    store_rows<D, O32>(p.dk, row, hh, dk, p.scale);
-    store_rows<D, O32>(p.dv, row, hh, dv, 1.0f);
+    if (p.n_gsplits == 1) {
+      store_rows<D, O32>(p.dk, row, hh, dk, p.scale);
+      store_rows<D, O32>(p.dv, row, hh, dv, 1.0f);
+    } else {
+      const size_t part = static_cast<size_t>(gs) * p.part_stride;
+      store_rows<D, true>(p.dk_part + part, row, hh, dk, p.scale);
+      store_rows<D, true>(p.dv_part + part, row, hh, dv, 1.0f);
+    }
+  }
+}
+
+// dK or dV from the fp32 partials of the n_gsplits query-head ranges:
+// out[e] = sum over s of part[s][e], in increasing s.
+template <bool O32>
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float *part,
+                                                           size_t stride,
+                                                           int n_parts,
+                                                           size_t n_vec4,
+                                                           void *out) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n_vec4;
+       i += static_cast<size_t>(gridDim.x) * 256) {
+    f32x4 acc = reinterpret_cast<const f32x4 *>(part)[i];
+    for (int s = 1; s < n_parts; ++s) {
+      const f32x4 x = reinterpret_cast<const f32x4 *>(part + s * stride)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += x[e];
+    }
+    if (O32) {
+      reinterpret_cast<f32x4 *>(out)[i] = acc;
+    } else {
+      __bf16 v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(acc[e]);
+      reinterpret_cast<u32x2 *>(out)[i] = __builtin_bit_cast(u32x2, v);
+    }
   }
 }
 
@@ -403,6 +469,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdParams p) {
   const int qb = CAUSAL ? (p.n_blocks - 1 - qbl) : qbl;  // longest first
   const int N = p.n;
   const size_t head = static_cast<size_t>(bh) * N * D;
+  const size_t kvhead = static_cast<size_t>(kv_head(bh, p.h, p.group)) * N * D;
   const int head_bytes = N * D * 2;
   const int q0 = qb * kBlk;
   const int qw = q0 + 32 * wv;
@@ -422,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[ct][r] = 0.f;
 
-  const uint16_t *kh = p.k + head, *vh = p.v + head;
+  const uint16_t *kh = p.k + kvhead, *vh = p.v + kvhead;
   const TileOffsets<D> off = tile_offsets<D>(lane, wv);
 
   const int kend = CAUSAL ? min(N, q0 + kBlk) : N;
@@ -494,10 +561,21 @@ hipError_t launch(const BwdParams &prm, int64_t rows, hipStream_t s) {
                      0, s, prm.o, prm.dout, prm.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, O32>), dim3(prm.total), dim3(kThreads),
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, O32>), dim3(prm.total_kv), dim3(kThreads),
                      0, s, prm);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (prm.n_gsplits > 1) {
+    const size_t n_vec4 = prm.part_stride / 4;
+    const size_t blocks = std::min<size_t>((n_vec4 + 255) / 256, 8192);
+    for (int i = 0; i < 2; ++i) {
+      hipLaunchKernelGGL((reduce_parts_kernel<O32>), dim3(blocks), dim3(256), 0, s,
+                         i == 0 ? prm.dk_part : prm.dv_part, prm.part_stride,
+                         prm.n_gsplits, n_vec4, i == 0 ? prm.dk : prm.dv);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   hipLaunchKernelGGL((dq_kernel<D, CAUSAL, O32>), dim3(prm.total), dim3(kThreads),
                      0, s, prm);
   return hipGetLastError();
@@ -528,6 +606,14 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, bool o32, hipStream_t s) {
   prm.n = a.n;
   prm.n_blocks = (a.n + kBlk - 1) / kBlk;
   prm.total = a.bh * prm.n_blocks;
+  prm.h = a.h;
+  prm.group = a.group;
+  prm.n_gsplits = a.n_gsplits;
+  prm.total_kv = a.bh / a.group * a.n_gsplits * prm.n_blocks;
+  prm.part_stride = static_cast<size_t>(a.bh / a.group) * a.n * a.d;
+  prm.dk_part = a.dkv_part;
+  prm.dv_part = a.dkv_part ? a.dkv_part + static_cast<size_t>(a.n_gsplits) * prm.part_stride
+                           : nullptr;
   prm.c = a.scale * kLog2e;
   prm.scale = a.scale;
   const int64_t rows = static_cast<int64_t>(a.bh) * a.n;

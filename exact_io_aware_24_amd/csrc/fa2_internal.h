@@ -29,11 +29,19 @@ struct FwdArgs {
 
 // Arguments of the backward pass (device pointers, validated shapes).
 struct BwdArgs {
-  const void *q, *k, *v, *o, *dout;  // [B*H][N][d] bf16
+  const void *q, *o, *dout;          // [B*H][N][d] bf16
+  const void *k, *v;                 // [B*H_kv][N][d] bf16
   const float *lse;                  // [B*H][N]
   float *delta;                      // [B*H][N], written
-  void *dq, *dk, *dv;                // [B*H][N][d], written
-  int bh;
+  void *dq;                          // [B*H][N][d], written
+  void *dk, *dv;                     // [B*H_kv][N][d], written
+  int bh;                            // B*H
+  int h;                             // H, query heads per batch index
+  int group;                         // H / H_kv (1: no shared K/V heads)
+  int n_gsplits;                     // ranges of a group's query heads whose
+                                     // dK/dV sums separate workgroups compute
+  float *dkv_part;                   // [2][n_gsplits][B*H_kv][N][d] fp32
+                                     // (n_gsplits > 1)
   int n;
   int d;
   float scale;

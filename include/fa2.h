@@ -247,11 +247,50 @@ int fa2_bwd_o32(const void *q, const void *k, const void *v, const void *o,
                 float *dk, float *dv, int B, int H, int N, int d, float scale,
                 int causal, void *stream);
 
+/*
+ * fa2_bwd_gqa -- gradients of fa2_fwd_gqa (H_kv <= H key/value heads shared
+ * by groups of H / H_kv consecutive query heads; grouped-query and
+ * multi-query attention, listed among FlashAttention-2's additions on the
+ * unite.ai page "Flash Attention: revolutionising transformer efficiency",
+ * section "FlashAttention-2").
+ *   q, o, dout, dq : [B][H][N][d];  k, v, dk, dv : [B][H_kv][N][d]
+ *   lse, delta     : [B][H][N], as for fa2_bwd
+ *   H_kv      : >= 1 and dividing H (else FA2_ERR_SHAPE)
+ *   n_gsplits : 1 .. H / H_kv (else FA2_ERR_SHAPE).  The dk/dv of a shared
+ *               head sum over its group of query heads; the group is cut
+ *               into n_gsplits ranges of consecutive heads computed by
+ *               separate workgroups (more parallel work when B * H_kv is
+ *               small), whose fp32 partial sums a last kernel adds in range
+ *               order.  1 = one workgroup per key block takes the whole
+ *               group, no partials.
+ *   dkv_part  : float [2][n_gsplits][B][H_kv][N][d] workspace owned by the
+ *               caller (dk partials, then dv partials), required when
+ *               n_gsplits > 1 (else FA2_ERR_NULL), ignored otherwise; it
+ *               may overlap no other argument (FA2_ERR_ALIAS)
+ * Same formulas, dtypes, rounding, stream order and error rules as fa2_bwd;
+ * with H_kv == H and n_gsplits == 1 it runs exactly fa2_bwd's kernels.
+ * Results are bit-reproducible for a given n_gsplits; different n_gsplits
+ * add the same fp32 terms in a different order.
+ */
+int fa2_bwd_gqa(const void *q, const void *k, const void *v, const void *o,
+                const void *dout, const float *lse, float *delta, void *dq,
+                void *dk, void *dv, int B, int H, int H_kv, int N, int d,
+                float scale, int causal, int n_gsplits, float *dkv_part,
+                void *stream);
+
+/* fa2_bwd_gqa_o32 -- fa2_bwd_gqa with float dq, dk, dv. */
+int fa2_bwd_gqa_o32(const void *q, const void *k, const void *v,
+                    const void *o, const void *dout, const float *lse,
+                    float *delta, float *dq, float *dk, float *dv, int B,
+                    int H, int H_kv, int N, int d, float scale, int causal,
+                    int n_gsplits, float *dkv_part, void *stream);
+
 /* Static English description of a return code (never NULL). */
 const char *fa2_strerror(int code);
 
-/* Library ABI version: 5 (2 added the backward pass, 3 grouped K/V heads,
-   4 split key ranges with separate query and key lengths, 5 the FP8 path). */
+/* Library ABI version: 6 (2 added the backward pass, 3 grouped K/V heads,
+   4 split key ranges with separate query and key lengths, 5 the FP8 path,
+   6 the grouped-head backward). */
 int fa2_version(void);
 
 #ifdef __cplusplus

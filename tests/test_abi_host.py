@@ -50,7 +50,7 @@ def test_codes_match_header():
 
 
 def test_version_and_strerror(L):
-    assert fa2.version() == 5
+    assert fa2.version() == 6
     seen = set()
     for name, code in header_codes().items():
         msg = fa2.strerror(code)
@@ -184,6 +184,53 @@ def test_bwd_binding_checks():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         fa2.backward(q, q, q, q, q, torch.zeros(1, 1, 8))
+
+
+# Grouped-head backward: K/V (and dK/dV) with H_kv heads, query-head ranges
+# with a partial-sum workspace
+GBWD_FUNCS = ("fa2_bwd_gqa", "fa2_bwd_gqa_o32")
+GBWD_NAMES = BWD_NAMES + ("part",)
+GBWD_GOOD = {name: 0x10000000 + i * 64 * MiB for i, name in enumerate(GBWD_NAMES)}
+
+
+def call_gbwd(fn, ptrs=None, B=1, H=8, H_kv=2, N=64, d=64, scale=0.125,
+              causal=1, n_gsplits=2):
+    p = dict(GBWD_GOOD)
+    p.update(ptrs or {})
+    return fa2.raw_call_bwd_gqa(fn, [p[n] for n in BWD_NAMES], B, H, H_kv, N, d,
+                                scale, causal, n_gsplits, p["part"])
+
+
+@pytest.mark.parametrize("fn", GBWD_FUNCS)
+def test_bwd_gqa_validation(L, fn):
+    for kw in (dict(H_kv=0), dict(H_kv=3), dict(H=2, H_kv=4), dict(n_gsplits=0),
+               dict(n_gsplits=5), dict(H_kv=8, n_gsplits=2), dict(N=0)):
+        assert call_gbwd(fn, **kw) == fa2.FA2_ERR_SHAPE, kw
+    for name in GBWD_NAMES:
+        assert call_gbwd(fn, {name: None}) == fa2.FA2_ERR_NULL, name
+    # one range: no workspace needed
+    assert call_gbwd(fn, {"part": None, "q": None}, n_gsplits=1) == fa2.FA2_ERR_NULL
+    assert call_gbwd(fn, d=96) == fa2.FA2_ERR_HEADDIM
+    assert call_gbwd(fn, scale=float("nan")) == fa2.FA2_ERR_SCALE
+    for name in GBWD_NAMES:
+        assert call_gbwd(fn, {name: GBWD_GOOD[name] + 4}) == fa2.FA2_ERR_ALIGN, name
+    # the workspace against every other buffer; dk/dv spans are H_kv heads
+    for other in BWD_NAMES:
+        assert call_gbwd(fn, {"part": GBWD_GOOD[other] + 16}) == fa2.FA2_ERR_ALIAS, other
+    # k is 1*2*64*64 bf16 = 16 KiB: dq right after it is fine, inside it is not
+    assert call_gbwd(fn, {"dq": GBWD_GOOD["k"] + 16 * 1024 - 16}) == fa2.FA2_ERR_ALIAS
+    # workspace = 2 * 2 * (1*2*64*64) fp32 = 128 KiB
+    assert call_gbwd(fn, {"dv": GBWD_GOOD["part"] + 128 * 1024 - 16}) == fa2.FA2_ERR_ALIAS
+
+
+def test_default_gsplits():
+    # B * H_kv * key blocks = 2 * 2 * 64 = 256 units -> 4 ranges of a group of 8
+    assert fa2.default_gsplits(2, 16, 2, 8192) == 4
+    # never more ranges than query heads per K/V head
+    assert fa2.default_gsplits(1, 4, 1, 1024) == 4
+    assert fa2.default_gsplits(1, 4, 4, 1024) == 1
+    # already enough workgroups
+    assert fa2.default_gsplits(8, 32, 8, 16384) == 1
 
 
 # Grouped-query forward: H_kv K/V heads
