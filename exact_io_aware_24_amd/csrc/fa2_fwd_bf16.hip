@@ -70,6 +70,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fa2_device.h"
@@ -95,7 +96,8 @@ struct Params {
   int n_qblocks;         // ceil(nq / 128)
   int n_splits;          // key ranges per query block (1: no split)
   int tiles_per_split;   // key tiles per range
-  int total;             // bh * n_qblocks * n_splits (grid size)
+  int total;             // bh * n_qblocks * n_splits (work items)
+  int persist;           // 1: the grid walks the items (see the kernel)
   size_t o_split_stride;    // elements between the partial outputs of splits
   size_t lse_split_stride;  // same for lse
   float c;               // scale * log2(e)
@@ -323,36 +325,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int lr = lane & 31;  // query column of this lane in S^T / O^T
   const int hh = lane >> 5;  // half-wave
 
-  // ---- workgroup -> (head, query block, key range) -------------------------
-  int logical = xcd_remap(blockIdx.x, p.total);
-  int split = 0;
-  if (p.n_splits > 1) {
-    split = logical % p.n_splits;
-    logical /= p.n_splits;
-  }
-  const int bh = logical / p.n_qblocks;
-  const int qbl = logical - bh * p.n_qblocks;
-  const int qb = CAUSAL ? (p.n_qblocks - 1 - qbl) : qbl;
-
   const int Nq = p.nq, Nk = p.nk;
   // causal: query i sits at key position i + Nk - Nq (the last query sees
   // every key; with Nq == Nk, query i sees keys 0..i)
   const int qoff = Nk - Nq;
-  const size_t qhead = static_cast<size_t>(bh) * Nq * D;
-  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(p.q + qhead), 0, Nq * D * 2, kBufWord3);
-  // K/V head shared by `group` consecutive query heads (grouped-query
-  // attention; 1 = one K/V head per query head)
-  const int kvbh = p.group == 1 ? bh : (bh / p.h) * (p.h / p.group) + (bh % p.h) / p.group;
-  const size_t kvhead = static_cast<size_t>(kvbh) * Nk * D;
   const int head_bytes = Nk * D * 2;  // < 2^31 (host-validated)
-  const uint16_t *kh = p.k + kvhead;
-  const uint16_t *vh = p.v + kvhead;
-
-  const int q0 = qb * kRows;      // first query of the block
-  const int qw = q0 + wv * 32;    // first query of this wave
-  const int qi = qw + lr;         // this lane's query
-  const int qpos = qi + qoff;     // its position among the keys
 
   // ---- fixed offsets -------------------------------------------------------
   Offsets<D> off;
@@ -379,162 +356,263 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       off.v_ld[it] = (16 * (kb0 + it) + lane / 4) * D * 2 + (4 * cg + (lane & 3)) * 16;
   }
 
-  // ---- Q into registers (B operand of S^T = K Q^T) -------------------------
-  WaveState<D> st;
   float c = p.c;
   uint32_t qflip = 0;
   if (c < 0.f) {  // exact: negate q (bf16 sign bit) and use -c
     c = -c;
     qflip = 0x80008000u;
   }
-  const int q_ld = (qi * D + 8 * hh) * 2;
-#pragma unroll
-  for (int t = 0; t < C::NDT; ++t) {
-    u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, q_ld + 32 * t, 0, 0);
-    x ^= qflip;
-    st.qreg[t] = __builtin_bit_cast(bf16x8, x);
-  }
-#pragma unroll
-  for (int ct = 0; ct < C::NCT; ++ct)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.oacc[ct][r] = 0.f;
-  st.m_run = -INFINITY;
-  st.l_run = 0.f;
-
-  // ---- tile schedule -------------------------------------------------------
-  // Software pipeline: iteration t computes the scores of tile t+1 (K one tile
-  // ahead in LDS) while it runs the softmax of tile t and the P.V product
-  // with V(t); the loads of K(t+2) and V(t+1) are in flight meanwhile.
-  // Tiles are numbered over the whole key range; this workgroup takes tiles
-  // [tb, ntiles) of it (all of them unless the keys are split).  Tiles below
-  // n_full need no mask for any row of the block; the rest (the diagonal
-  // band when causal, the ragged end of the keys) are masked.
-  const int kend = CAUSAL ? max(0, min(Nk, q0 + kRows + qoff)) : Nk;
-  const int tb = split * p.tiles_per_split;
-  const int ntiles = min((kend + C::BC - 1) / C::BC, tb + p.tiles_per_split);
-  const int n_full = CAUSAL ? max(0, (q0 + qoff + 1) / C::BC) : Nk / C::BC;
-  // waves with no query rows (short query blocks) only help with the loads
-  const bool live = qw < Nq;
-  // tiles this wave needs (causal: keys up to its last query)
-  const int w_tiles = !live ? tb
-                      : CAUSAL ? min(ntiles, (qw + 31 + qoff) / C::BC + 1) : ntiles;
-  // branch-free main loop: tiles t and t+1 unmasked
-  const int n_main = live ? min(n_full, ntiles) - 1 : tb;
 
   auto kbuf = [&](int i) { return smem + i * C::TILE_BYTES; };
   auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE_BYTES; };
-  f32x16 sa[C::NKT], sb[C::NKT];
 
-  // Rows past the end of the sequence load as zeros; clear LDS first so that
-  // no tile can ever expose uninitialised bits, whatever the hardware does
-  // with out-of-range lanes.
-  if (tb < ntiles) {  // (an empty key range leaves l = 0: O = 0, lse = -inf)
-  if (Nk % C::BC != 0) {
-    for (int i = tid; i < 4 * C::TILE_BYTES / 16; i += kThreads)
-      reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-  }
-  // prologue: K(tb), V(tb) -> buffers 0; then K(tb+1) in flight while S(tb)
-  // is computed.  Buffer parity is (t - tb) & 1.
-  issue_k<D>(kh, head_bytes, off, kbuf(0), wv, tb * C::BC * D * 2);
-  issue_v<D>(vh, head_bytes, off, vbuf(0), wv, tb * C::BC * D * 2);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tb + 1 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(1), wv, (tb + 1) * C::BC * D * 2);
-  if (tb < w_tiles) {
-    scores<D>(kbuf(0), off, st.qreg, sa);
-    if (tb < n_full)
-      softmax_max<D, CAUSAL, false>(sa, st, c, tb * C::BC, Nk, qpos, hh);
-    else
-      softmax_max<D, CAUSAL, true>(sa, st, c, tb * C::BC, Nk, qpos, hh);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // one pipelined iteration; CUR holds S(t), NXT receives S(t+1)
-  auto step = [&](auto par_tag, int t, f32x16(&cur)[C::NKT],
-                  f32x16(&nxt)[C::NKT]) {
-    constexpr int P = decltype(par_tag)::value;  // (t - tb) & 1
-    const int j0 = t * C::BC;
-    if (t + 2 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(P), wv, (j0 + 2 * C::BC) * D * 2);
-    issue_v<D>(vh, head_bytes, off, vbuf(1 - P), wv, (j0 + C::BC) * D * 2);
-    scores<D>(kbuf(1 - P), off, st.qreg, nxt);
-    bf16x8 pb[C::NKT][2];
-    softmax_exp<D, false>(cur, st.m_run, c, pb, st.l_run);
-    pv<D>(vbuf(P), off, pb, st.oacc);
-    softmax_max<D, CAUSAL, false>(nxt, st, c, j0 + C::BC, Nk, qpos, hh);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // ---- work items ----------------------------------------------------------
+  // An item is (batch*head, query block, key range).  Without p.persist each
+  // workgroup takes one item, ids remapped so that each XCD runs a
+  // contiguous range of them.  With it, a grid of two workgroups per compute
+  // unit walks the items: the workgroups of XCD x (hardware deals workgroup
+  // w to XCD w % 8) take the contiguous items [x*total/8, (x+1)*total/8),
+  // workgroup j of the XCD item r*per + j in round r, the order reversed on
+  // odd rounds so that a long causal block is paired with a short one.  The
+  // loads of an item's first tiles and of its Q rows are then issued during
+  // the last tile of the item before (see the general loop).
+  const int per = static_cast<int>(gridDim.x >> 3);
+  const int xj = static_cast<int>(blockIdx.x >> 3);
+  const int xcd = static_cast<int>(blockIdx.x & 7);
+  const int ilo = static_cast<int>(static_cast<int64_t>(xcd) * p.total / 8);
+  const int ilen = static_cast<int>(static_cast<int64_t>(xcd + 1) * p.total / 8) - ilo;
+  // (d = 64 never walks: the item loop's extra live registers would spill)
+  constexpr bool kCanPersist = D == 128;
+  auto item_at = [&](int r) -> int {
+    if (!kCanPersist || !p.persist) return r == 0 ? xcd_remap(blockIdx.x, p.total) : -1;
+    const int local = r * per + ((r & 1) ? per - 1 - xj : xj);
+    return local < ilen ? ilo + local : -1;
   };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-
-  int t = tb;
-  for (; t + 2 <= n_main; t += 2) {
-    step(P0{}, t, sa, sb);
-    step(P1{}, t + 1, sb, sa);
-  }
-  if (t < n_main) {
-    step(P0{}, t, sa, sb);
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) sa[kt] = sb[kt];
-    ++t;
-  }
-  // general loop: masked tiles, waves that stop early, the last tile
-  for (; t < ntiles; ++t) {
-    const int j0 = t * C::BC;
-    const int p = (t - tb) & 1;
-    if (t + 2 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(p), wv, (j0 + 2 * C::BC) * D * 2);
-    if (t + 1 < ntiles) issue_v<D>(vh, head_bytes, off, vbuf(1 - p), wv, (j0 + C::BC) * D * 2);
-    if (t + 1 < w_tiles) scores<D>(kbuf(1 - p), off, st.qreg, sb);
-    if (t < w_tiles) {
-      const float mu = (st.m_run == -INFINITY) ? 0.f : st.m_run;
-      bf16x8 pb[C::NKT][2];
-      softmax_exp<D, true>(sa, mu, c, pb, st.l_run);
-      pv<D>(vbuf(p), off, pb, st.oacc);
+  // item -> key range, batch*head, first query row
+  auto decode = [&](int logical, int &split, int &bh, int &q0) {
+    split = 0;
+    if (p.n_splits > 1) {
+      split = logical % p.n_splits;
+      logical /= p.n_splits;
     }
-    if (t + 1 < w_tiles)
-      softmax_max<D, CAUSAL, true>(sb, st, c, j0 + C::BC, Nk, qpos, hh);
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) sa[kt] = sb[kt];
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  }  // tb < ntiles
+    bh = logical / p.n_qblocks;
+    const int qbl = logical - bh * p.n_qblocks;
+    q0 = (CAUSAL ? (p.n_qblocks - 1 - qbl) : qbl) * kRows;
+  };
+  // K/V head shared by `group` consecutive query heads (grouped-query
+  // attention; 1 = one K/V head per query head)
+  auto kv_head = [&](int bh) -> size_t {
+    const int kvbh = p.group == 1 ? bh : (bh / p.h) * (p.h / p.group) + (bh % p.h) / p.group;
+    return static_cast<size_t>(kvbh) * Nk * D;
+  };
+  // key tiles the query block starting at q0 needs (causal: up to its last query)
+  auto block_tiles = [&](int q0) -> int {
+    const int kend = CAUSAL ? max(0, min(Nk, q0 + kRows + qoff)) : Nk;
+    return (kend + C::BC - 1) / C::BC;
+  };
 
-  // ---- epilogue: O = O~ / l, lse ---------------------------------------------
-  float llo, lhi;
-  halves(st.l_run, llo, lhi);
-  const float l_tot = llo + lhi;
-  // a row that saw no key (only possible within one key range of a split,
-  // or causal with more queries than keys): O = 0, lse = -inf
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (qi < Nq) {
-    const size_t head = qhead + split * p.o_split_stride;
-    // O^T register r of row tile ct holds column 32ct + 8(r/4) + 4hh + r%4
+  // Q into registers (B operand of S^T = K Q^T); the sign flip of a negative
+  // scale is applied at the start of the item, once the rows have arrived
+  WaveState<D> st;
+  auto load_q = [&](int bh, int q0) {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.q + static_cast<size_t>(bh) * Nq * D), 0, Nq * D * 2,
+        kBufWord3);
+    const int q_ld = ((q0 + wv * 32 + lr) * D + 8 * hh) * 2;
+#pragma unroll
+    for (int t = 0; t < C::NDT; ++t)
+      st.qreg[t] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, q_ld + 32 * t, 0, 0));
+  };
+
+  bool pre = false;  // this item's Q, K/V(0) and K(1) were issued already
+  bool handed = false;
+  int logical = item_at(0);
+  for (int r = 0; logical >= 0; ++r) {
+    const int nxt = item_at(r + 1);
+    int split, bh, q0;
+    decode(logical, split, bh, q0);
+    const size_t qhead = static_cast<size_t>(bh) * Nq * D;
+    const size_t kvhead = kv_head(bh);
+    const uint16_t *kh = p.k + kvhead;
+    const uint16_t *vh = p.v + kvhead;
+    const int qw = q0 + wv * 32;    // first query of this wave
+    const int qi = qw + lr;         // this lane's query
+    const int qpos = qi + qoff;     // its position among the keys
+
+    if (!pre) load_q(bh, q0);
+#pragma unroll
+    for (int t = 0; t < C::NDT; ++t)
+      st.qreg[t] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, st.qreg[t]) ^ qflip);
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int col = 32 * ct + 8 * a + 4 * hh;
-        const size_t o_off = head + static_cast<size_t>(qi) * D + col;
-        if (O32) {
-          f32x4 ov;
+      for (int r2 = 0; r2 < 16; ++r2) st.oacc[ct][r2] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    // ---- tile schedule -----------------------------------------------------
+    // Software pipeline: iteration t computes the scores of tile t+1 (K one
+    // tile ahead in LDS) while it runs the softmax of tile t and the P.V
+    // product with V(t); the loads of K(t+2) and V(t+1) are in flight
+    // meanwhile.  Tiles are numbered over the whole key range; this item
+    // takes tiles [tb, ntiles) of it (all of them unless the keys are split).
+    // Tiles below n_full need no mask for any row of the block; the rest (the
+    // diagonal band when causal, the ragged end of the keys) are masked.
+    const int tb = split * p.tiles_per_split;
+    const int ntiles = min(block_tiles(q0), tb + p.tiles_per_split);
+    const int n_full = CAUSAL ? max(0, (q0 + qoff + 1) / C::BC) : Nk / C::BC;
+    // waves with no query rows (short query blocks) only help with the loads
+    const bool live = qw < Nq;
+    // tiles this wave needs (causal: keys up to its last query)
+    const int w_tiles = !live ? tb
+                        : CAUSAL ? min(ntiles, (qw + 31 + qoff) / C::BC + 1) : ntiles;
+    // branch-free main loop: tiles t and t+1 unmasked
+    const int n_main = live ? min(n_full, ntiles) - 1 : tb;
+    f32x16 sa[C::NKT], sb[C::NKT];
+
+    if (tb < ntiles) {  // (an empty key range leaves l = 0: O = 0, lse = -inf)
+    // Rows past the end of the sequence load as zeros; clear LDS first so
+    // that no tile can ever expose uninitialised bits, whatever the hardware
+    // does with out-of-range lanes.  (Never with p.persist.)
+    if (Nk % C::BC != 0) {
+      for (int i = tid; i < 4 * C::TILE_BYTES / 16; i += kThreads)
+        reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
+    // prologue: K(tb), V(tb) -> buffers 0; then K(tb+1) in flight while S(tb)
+    // is computed.  Buffer parity is (t - tb) & 1.
+    if (!pre) {
+      issue_k<D>(kh, head_bytes, off, kbuf(0), wv, tb * C::BC * D * 2);
+      issue_v<D>(vh, head_bytes, off, vbuf(0), wv, tb * C::BC * D * 2);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (!pre && tb + 1 < ntiles)
+      issue_k<D>(kh, head_bytes, off, kbuf(1), wv, (tb + 1) * C::BC * D * 2);
+    if (tb < w_tiles) {
+      scores<D>(kbuf(0), off, st.qreg, sa);
+      if (tb < n_full)
+        softmax_max<D, CAUSAL, false>(sa, st, c, tb * C::BC, Nk, qpos, hh);
+      else
+        softmax_max<D, CAUSAL, true>(sa, st, c, tb * C::BC, Nk, qpos, hh);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // one pipelined iteration; CUR holds S(t), NXT receives S(t+1)
+    auto step = [&](auto par_tag, int t, f32x16(&cur)[C::NKT],
+                    f32x16(&nxt)[C::NKT]) {
+      constexpr int P = decltype(par_tag)::value;  // (t - tb) & 1
+      const int j0 = t * C::BC;
+      if (t + 2 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(P), wv, (j0 + 2 * C::BC) * D * 2);
+      issue_v<D>(vh, head_bytes, off, vbuf(1 - P), wv, (j0 + C::BC) * D * 2);
+      scores<D>(kbuf(1 - P), off, st.qreg, nxt);
+      bf16x8 pb[C::NKT][2];
+      softmax_exp<D, false>(cur, st.m_run, c, pb, st.l_run);
+      pv<D>(vbuf(P), off, pb, st.oacc);
+      softmax_max<D, CAUSAL, false>(nxt, st, c, j0 + C::BC, Nk, qpos, hh);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+
+    int t = tb;
+    for (; t + 2 <= n_main; t += 2) {
+      step(P0{}, t, sa, sb);
+      step(P1{}, t + 1, sb, sa);
+    }
+    if (t < n_main) {
+      step(P0{}, t, sa, sb);
 #pragma unroll
-          for (int b = 0; b < 4; ++b) ov[b] = st.oacc[ct][4 * a + b] * inv;
-          *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + o_off) = ov;
-        } else {
-          __bf16 ob[4];
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            ob[b] = static_cast<__bf16>(st.oacc[ct][4 * a + b] * inv);
-          *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p.o) + o_off) =
-              __builtin_bit_cast(u32x2, ob);
+      for (int kt = 0; kt < C::NKT; ++kt) sa[kt] = sb[kt];
+      ++t;
+    }
+    // general loop: masked tiles, waves that stop early, the last tile.  In
+    // the last tile no K buffer is read and only V buffer p is, so the next
+    // item's Q rows, K(0), K(1) and (when p == 1) V(0) are issued there;
+    // that iteration then skips its wait for loads, which the next item's
+    // prologue waits for.  (Items start at tile 0 when p.persist is set.)
+    bool v_next = false;  // V(0) of the next item issued
+    for (; t < ntiles; ++t) {
+      const int j0 = t * C::BC;
+      const int pr = (t - tb) & 1;
+      const bool hand_over = nxt >= 0 && t + 1 == ntiles;
+      if (t + 2 < ntiles) issue_k<D>(kh, head_bytes, off, kbuf(pr), wv, (j0 + 2 * C::BC) * D * 2);
+      if (t + 1 < ntiles) issue_v<D>(vh, head_bytes, off, vbuf(1 - pr), wv, (j0 + C::BC) * D * 2);
+      if (t + 1 < w_tiles) scores<D>(kbuf(1 - pr), off, st.qreg, sb);
+      if (hand_over) {
+        int split2, bh2, q02;
+        decode(nxt, split2, bh2, q02);
+        load_q(bh2, q02);
+        const size_t kv2 = kv_head(bh2);
+        issue_k<D>(p.k + kv2, head_bytes, off, kbuf(0), wv, 0);
+        if (block_tiles(q02) > 1)
+          issue_k<D>(p.k + kv2, head_bytes, off, kbuf(1), wv, C::BC * D * 2);
+        if (pr == 1) {
+          issue_v<D>(p.v + kv2, head_bytes, off, vbuf(0), wv, 0);
+          v_next = true;
         }
+        handed = true;
       }
-    if (p.lse && hh == 0)
-      p.lse[split * p.lse_split_stride + static_cast<size_t>(bh) * Nq + qi] =
-          l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      if (t < w_tiles) {
+        const float mu = (st.m_run == -INFINITY) ? 0.f : st.m_run;
+        bf16x8 pb[C::NKT][2];
+        softmax_exp<D, true>(sa, mu, c, pb, st.l_run);
+        pv<D>(vbuf(pr), off, pb, st.oacc);
+      }
+      if (t + 1 < w_tiles)
+        softmax_max<D, CAUSAL, true>(sb, st, c, j0 + C::BC, Nk, qpos, hh);
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt) sa[kt] = sb[kt];
+      if (!hand_over) __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (nxt >= 0 && !v_next) {  // V buffer 0 was read by the last tile
+      int split2, bh2, q02;
+      decode(nxt, split2, bh2, q02);
+      issue_v<D>(p.v + kv_head(bh2), head_bytes, off, vbuf(0), wv, 0);
+    }
+    }  // tb < ntiles
+
+    // ---- epilogue: O = O~ / l, lse -------------------------------------------
+    float llo, lhi;
+    halves(st.l_run, llo, lhi);
+    const float l_tot = llo + lhi;
+    // a row that saw no key (only possible within one key range of a split,
+    // or causal with more queries than keys): O = 0, lse = -inf
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if (qi < Nq) {
+      const size_t head = qhead + split * p.o_split_stride;
+      // O^T register r of row tile ct holds column 32ct + 8(r/4) + 4hh + r%4
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int col = 32 * ct + 8 * a + 4 * hh;
+          const size_t o_off = head + static_cast<size_t>(qi) * D + col;
+          if (O32) {
+            f32x4 ov;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) ov[b] = st.oacc[ct][4 * a + b] * inv;
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + o_off) = ov;
+          } else {
+            __bf16 ob[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              ob[b] = static_cast<__bf16>(st.oacc[ct][4 * a + b] * inv);
+            *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p.o) + o_off) =
+                __builtin_bit_cast(u32x2, ob);
+          }
+        }
+      if (p.lse && hh == 0)
+        p.lse[split * p.lse_split_stride + static_cast<size_t>(bh) * Nq + qi] =
+            l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    logical = nxt;
+    pre = handed;
+    handed = false;
   }
 }
 
@@ -586,17 +664,33 @@ __global__ __launch_bounds__(kThreads) void merge_splits_kernel(
 }
 
 template <int D, bool CAUSAL, bool O32>
-hipError_t launch(const Params &prm, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, O32>), dim3(prm.total),
+hipError_t launch(const Params &prm, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, O32>), dim3(grid),
                      dim3(kThreads), 0, s, prm);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const Params &prm, bool causal, bool o32, hipStream_t s) {
+hipError_t launch_d(const Params &prm, int grid, bool causal, bool o32, hipStream_t s) {
   if (causal)
-    return o32 ? launch<D, true, true>(prm, s) : launch<D, true, false>(prm, s);
-  return o32 ? launch<D, false, true>(prm, s) : launch<D, false, false>(prm, s);
+    return o32 ? launch<D, true, true>(prm, grid, s) : launch<D, true, false>(prm, grid, s);
+  return o32 ? launch<D, false, true>(prm, grid, s) : launch<D, false, false>(prm, grid, s);
+}
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <int D>
@@ -634,20 +728,37 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s) {
   prm.tiles_per_split = (key_tiles + a.n_splits - 1) / a.n_splits;
   prm.total = a.bh * prm.n_qblocks * a.n_splits;
   prm.c = a.scale * kLog2e;
+  // A grid of two workgroups per compute unit walks the items when there
+  // are more items than that and every item starts at key tile 0 with whole
+  // tiles (d = 128, one key range, equal query and key lengths, no ragged
+  // tile) -- and only for causal attention with at most 64 query blocks per
+  // head, where hiding each block's first loads and pairing long with short
+  // blocks measured faster.  Elsewhere (uniform blocks, or blocks so long
+  // that speed differences between workgroups outweigh the saved latency)
+  // the hardware's dynamic dispatch of one workgroup per item measured
+  // as fast or faster.
+  prm.persist = 0;
+  int grid = prm.total;
+  const int slots = (2 * cu_count()) & ~7;
+  if (a.d == 128 && a.causal && prm.n_qblocks <= 64 && a.n_splits == 1 &&
+      a.nq == a.nk && a.nk % bc == 0 && slots >= 8 && prm.total > slots) {
+    prm.persist = 1;
+    grid = slots;
+  }
   if (a.n_splits == 1) {
     prm.o = a.o;
     prm.lse = a.lse;
     prm.o_split_stride = prm.lse_split_stride = 0;
-    if (a.d == 128) return launch_d<128>(prm, a.causal, o32, s);
-    return launch_d<64>(prm, a.causal, o32, s);
+    if (a.d == 128) return launch_d<128>(prm, grid, a.causal, o32, s);
+    return launch_d<64>(prm, grid, a.causal, o32, s);
   }
   // key ranges into the fp32 partial buffers, then the merge
   prm.o = a.o_part;
   prm.lse = a.lse_part;
   prm.o_split_stride = static_cast<size_t>(a.bh) * a.nq * a.d;
   prm.lse_split_stride = static_cast<size_t>(a.bh) * a.nq;
-  hipError_t e = a.d == 128 ? launch_d<128>(prm, a.causal, true, s)
-                            : launch_d<64>(prm, a.causal, true, s);
+  hipError_t e = a.d == 128 ? launch_d<128>(prm, grid, a.causal, true, s)
+                            : launch_d<64>(prm, grid, a.causal, true, s);
   if (e != hipSuccess) return e;
   return a.d == 128 ? launch_merge<128>(a, o32, prm.o_split_stride, prm.lse_split_stride, s)
                     : launch_merge<64>(a, o32, prm.o_split_stride, prm.lse_split_stride, s);
