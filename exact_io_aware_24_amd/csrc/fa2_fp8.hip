@@ -60,60 +60,88 @@ __device__ __forceinline__ int cvt_fp8x4(float x0, float x1, float x2, float x3)
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, lo, true);
 }
 
-// One workgroup per (head, block of R rows).  D/8 lanes per row, 8 values
-// per lane; the transform's stages h < 8 are inside a lane, h >= 8 swap
-// values between the lanes of a row.
+// One workgroup per (head, block of R rows).  Four lanes per row, D/4
+// values per lane (contiguous): the transform's stages h < D/4 run inside a
+// lane, the last two (h = D/4, D/2) pair the lanes of a row, which form one
+// quad, exchanged by DPP quad permutes.  In a cross-lane butterfly the lane
+// holding the pair's upper element negates its value and adds its
+// partner's: b + (-a) is exactly b - a, the same fp32 operations in the
+// same order as the in-lane stages.
 template <int D, int R>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t *x, uint8_t *codes, int *exps, const float *signs, int n,
     int nblocks) {
-  constexpr int LPR = D / 8;
-  constexpr int RPP = kThreads / LPR;  // rows per pass
+  constexpr int EPL = D / 4;           // values per lane
+  constexpr int RPP = kThreads / 4;    // rows per pass
   constexpr int PASSES = R / RPP;
+  static_assert(PASSES >= 1 && R % RPP == 0, "block rows");
   __shared__ float wmax[kThreads / 64];
   const int bh = blockIdx.x / nblocks;
   const int blk = blockIdx.x - bh * nblocks;
-  const int part = threadIdx.x % LPR;
+  const int part = threadIdx.x & 3;
   const size_t head = static_cast<size_t>(bh) * n * D;
-  float sg[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sg[e] = signs ? signs[part * 8 + e] : 1.f;
-  float y[PASSES][8];
+  // sign flips of this lane's columns as a bit mask: ballots over the
+  // wave's lanes give columns 0-63 and 64-127, each lane takes its slice
+  uint32_t neg = 0;
+  if (signs) {
+    const int l = threadIdx.x & 63;
+    const uint64_t lo = __builtin_amdgcn_ballot_w64(signs[l] < 0.f);
+    uint64_t hi = 0;
+    if (D == 128) hi = __builtin_amdgcn_ballot_w64(signs[64 + l] < 0.f);
+    const uint64_t word = (part * EPL < 64) ? lo : hi;
+    neg = static_cast<uint32_t>(word >> ((part * EPL) & 63));
+    if (EPL < 32) neg &= (1u << EPL) - 1u;
+  }
+  float y[PASSES][EPL];
   float amax = 0.f;
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
-    const int row = blk * R + ps * RPP + threadIdx.x / LPR;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (row < n)
-      raw = *reinterpret_cast<const u32x4 *>(x + head + static_cast<size_t>(row) * D + part * 8);
+    const int row = blk * R + ps * RPP + (threadIdx.x >> 2);
+    u32x4 raw[EPL / 8];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      y[ps][2 * w] = __uint_as_float(raw[w] << 16) * sg[2 * w];
-      y[ps][2 * w + 1] = __uint_as_float(raw[w] & 0xffff0000u) * sg[2 * w + 1];
+    for (int c = 0; c < EPL / 8; ++c) raw[c] = u32x4{0u, 0u, 0u, 0u};
+    if (row < n) {
+#pragma unroll
+      for (int c = 0; c < EPL / 8; ++c)
+        raw[c] = *reinterpret_cast<const u32x4 *>(
+            x + head + static_cast<size_t>(row) * D + part * EPL + 8 * c);
     }
+#pragma unroll
+    for (int c = 0; c < EPL / 8; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        y[ps][8 * c + 2 * w] = __uint_as_float(raw[c][w] << 16);
+        y[ps][8 * c + 2 * w + 1] = __uint_as_float(raw[c][w] & 0xffff0000u);
+      }
     if (signs) {
 #pragma unroll
-      for (int h = 1; h < 8; h <<= 1)
+      for (int e = 0; e < EPL; ++e)
+        y[ps][e] = __uint_as_float(__float_as_uint(y[ps][e]) ^ (((neg >> e) & 1u) << 31));
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+      for (int h = 1; h < EPL; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
           if (!(i & h)) {
-            const float a = y[ps][i], b = y[ps][i + h];
-            y[ps][i] = a + b;
-            y[ps][i + h] = a - b;
+            const float a = y[ps][i], b2 = y[ps][i + h];
+            y[ps][i] = a + b2;
+            y[ps][i + h] = a - b2;
           }
+      // h = EPL: partner lane part ^ 1; h = 2 EPL: part ^ 2
 #pragma unroll
-      for (int h = 8; h < D; h <<= 1) {
-        const int m = h / 8;  // partner lane within the row
-        const bool upper = part & m;
+      for (int st = 0; st < 2; ++st) {
+        const bool upper = (part >> st) & 1;
+        const uint32_t flip = upper ? 0x80000000u : 0u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float other = __shfl_xor(y[ps][i], m, 64);
-          y[ps][i] = upper ? other - y[ps][i] : y[ps][i] + other;
+        for (int i = 0; i < EPL; ++i) {
+          const int mine = __float_as_int(y[ps][i]);
+          const int other = st == 0 ? __builtin_amdgcn_update_dpp(0, mine, 0xB1, 0xF, 0xF, false)
+                                    : __builtin_amdgcn_update_dpp(0, mine, 0x4E, 0xF, 0xF, false);
+          y[ps][i] = __int_as_float(other) + __uint_as_float(__float_as_uint(y[ps][i]) ^ flip);
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[ps][i]));
+    for (int i = 0; i < EPL; ++i) amax = fmaxf(amax, fabsf(y[ps][i]));
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
@@ -125,12 +153,20 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   if (threadIdx.x == 0) exps[static_cast<size_t>(bh) * nblocks + blk] = e;
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
-    const int row = blk * R + ps * RPP + threadIdx.x / LPR;
-    const int w0 = cvt_fp8x4(y[ps][0] * inv, y[ps][1] * inv, y[ps][2] * inv, y[ps][3] * inv);
-    const int w1 = cvt_fp8x4(y[ps][4] * inv, y[ps][5] * inv, y[ps][6] * inv, y[ps][7] * inv);
-    if (row < n)
-      *reinterpret_cast<u32x2 *>(codes + head + static_cast<size_t>(row) * D + part * 8) =
-          u32x2{static_cast<uint32_t>(w0), static_cast<uint32_t>(w1)};
+    const int row = blk * R + ps * RPP + (threadIdx.x >> 2);
+    u32x4 out[EPL / 16];
+#pragma unroll
+    for (int c = 0; c < EPL / 16; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float *v4 = &y[ps][16 * c + 4 * w];
+        out[c][w] = static_cast<uint32_t>(cvt_fp8x4(v4[0] * inv, v4[1] * inv, v4[2] * inv, v4[3] * inv));
+      }
+    if (row < n) {
+#pragma unroll
+      for (int c = 0; c < EPL / 16; ++c)
+        *reinterpret_cast<u32x4 *>(codes + head + static_cast<size_t>(row) * D + part * EPL + 16 * c) = out[c];
+    }
   }
 }
 
