@@ -53,6 +53,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "fa2_device.h"
 #include "fa2_internal.h"
@@ -350,16 +351,18 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
   __syncthreads();
 
   const float c = p.c;
-  // (head, tile) pairs head-major; the next pair's tile is prefetched
+  // One (head, tile) step, the next pair's tile prefetched (head-major
+  // order).  MASKED: the tile holds a query before one of the block's keys
+  // (causal, t < t_full) -- a compile-time switch, so that the other tiles
+  // carry no mask instructions.
   int b = 0;
-  for (int g = 0; g < ng; ++g)
-  for (int t = t0; t < nt; ++t, b ^= 1) {
+  auto step = [&](auto masked_tag, int g, int t) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     if (t + 1 < nt) issue(g, t + 1, b ^ 1);
     else if (g + 1 < ng) issue(g + 1, t0, b ^ 1);
     // this wave's keys all come after every query of the tile: nothing to do
     const bool skip = CAUSAL && (t * kTileRows + kTileRows - 1 < kw);
     if (!skip) {
-      const bool masked = CAUSAL && t < t_full;
       const char *qb = qbuf(b), *ob = obuf(b);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {  // 32-query halves of the tile
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * a + e;
             float x = fast_exp2(__builtin_fmaf(s[r], c, -l4[e] * kLog2e));
-            if (masked && kj > t * kTileRows + qrow + e) x = 0.f;
+            if (MASKED && kj > t * kTileRows + qrow + e) x = 0.f;
             const float ds = x * (dp[r] - d4[e]);
             pb[r >> 3][r & 7] = static_cast<__bf16>(x);
             sb[r >> 3][r & 7] = static_cast<__bf16>(ds);
@@ -399,6 +402,13 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    b ^= 1;
+  };
+  const int t_mask_end = CAUSAL ? min(t_full, nt) : t0;
+  for (int g = 0; g < ng; ++g) {
+    int t = t0;
+    for (; t < t_mask_end; ++t) step(std::true_type{}, g, t);
+    for (; t < nt; ++t) step(std::false_type{}, g, t);
   }
 
   if (kj < N) {
@@ -509,14 +519,17 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdParams p) {
   __syncthreads();
 
   const float c = p.c;
-  for (int t = 0; t < nt; ++t) {
+  // One tile; MASKED (the tiles from n_full on: the diagonal band, the
+  // ragged end) is a compile-time switch, so that the other tiles carry no
+  // mask instructions.
+  auto step = [&](auto masked_tag, int t) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int b = t & 1;
     if (t + 1 < nt) {
       issue_tile<D>(kh, head_bytes, off, kbuf(b ^ 1), wv, (t + 1) * kTileRows);
       issue_tile<D>(vh, head_bytes, off, vbuf(b ^ 1), wv, (t + 1) * kTileRows);
     }
     if (t < w_tiles) {
-      const bool masked = t >= n_full;
       const char *kbp = kbuf(b), *vbp = vbuf(b);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {  // 32-key halves of the tile
@@ -533,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float x = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
-          if (masked) {
+          if (MASKED) {
             const int key = t * kTileRows + 32 * h + 8 * (r >> 2) + 4 * hh + (r & 3);
             if (key >= N || (CAUSAL && key > qi)) x = 0.f;
           }
@@ -548,7 +561,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(BwdParams p) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  }
+  };
+  int t = 0;
+  for (; t < n_full; ++t) step(std::false_type{}, t);
+  for (; t < nt; ++t) step(std::true_type{}, t);
 
   if (qi < N)
     store_rows<D, O32>(p.dq, head + static_cast<size_t>(qi) * D, hh, dq, p.scale);
