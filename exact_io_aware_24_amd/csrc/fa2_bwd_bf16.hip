@@ -346,8 +346,18 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
       reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
   }
+  // Wave 0 stages each tile's lse; once its load has landed (its own wait),
+  // and before the barrier that publishes the tile, it turns the 64 values
+  // into base-2 units in place, so that no wave multiplies them per element.
+  auto lse_to_base2 = [&](int buf) {
+    if (wv == 0) {
+      float *l = reinterpret_cast<float *>(lbuf(buf)) + lane;
+      *l = *l * kLog2e;
+    }
+  };
   if (t0 < nt) issue(0, t0, 0);
   __builtin_amdgcn_s_waitcnt(0);
+  lse_to_base2(0);
   __syncthreads();
 
   const float c = p.c;
@@ -379,12 +389,12 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const int qrow = 32 * h + 8 * a + 4 * hh;
-          const f32x4 l4 = lds_load<f32x4>(lbuf(b), qrow * 4);
+          const f32x4 l4 = lds_load<f32x4>(lbuf(b), qrow * 4);  // lse log2(e)
           const f32x4 d4 = lds_load<f32x4>(dbuf(b), qrow * 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * a + e;
-            float x = fast_exp2(__builtin_fmaf(s[r], c, -l4[e] * kLog2e));
+            float x = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
             if (MASKED && kj > t * kTileRows + qrow + e) x = 0.f;
             const float ds = x * (dp[r] - d4[e]);
             pb[r >> 3][r & 7] = static_cast<__bf16>(x);
@@ -401,6 +411,7 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
+    if (t + 1 < nt || g + 1 < ng) lse_to_base2(b ^ 1);
     __syncthreads();
     b ^= 1;
   };
