@@ -289,74 +289,177 @@ int oracle_probs_f64(const double *q, const double *k, int64_t nq, int64_t nk,
  *   dQ_i  = scale * sum_j dS_ij K_j                (S_ij = scale Q_i . K_j)
  *   dK_j  = scale * sum_i dS_ij Q_i
  *
- * Masked entries have P_ij = 0 and so contribute nothing.  Everything is in
- * double precision, one query row at a time over all of its keys.  Rows are
- * split statically over the threads; each thread sums its rows' dK and dV
- * contributions privately and the partial sums are added in thread order,
- * so a given thread count always gives the same bits.
+ * Masked entries have P_ij = 0 and so contribute nothing: the sums below
+ * run over the visible pairs only (adding an exact zero changes no sum).
+ * Everything is in double precision.  Two passes, each over independent
+ * items split between threads:
+ *   rows:  for each query row i, P_i (with its m_i and l_i), dP_i, D_i and
+ *          dQ_i, every sum over the keys j in increasing order;
+ *   keys:  for each key j, dK_j and dV_j summed over the query rows i in
+ *          increasing order, with P_ij recomputed from the same operations
+ *          as in the row pass (the same bits) and D_i from that pass.
+ * No sum is split between threads, so the result does not depend on the
+ * thread count.
  */
 
 typedef struct {
     const double *q, *k, *v, *dout;
-    double *dq, *delta;
-    double *dk_part, *dv_part; /* this thread's [nk][d] partial sums */
-    int64_t r0, r1, nk, d;
+    double *dq, *dk, *dv, *delta;
+    double *m, *l;          /* [nh][nq] row statistics from the row pass */
+    int64_t nq, nk, d;
     double scale;
     int causal;
+    int keys;               /* 0: row pass, 1: key pass */
+    int64_t total, next;
+    pthread_mutex_t lock;
     int failed;
 } bwd_job_t;
+
+static int64_t bwd_claim(bwd_job_t *jb, int64_t chunk, int64_t *end)
+{
+    pthread_mutex_lock(&jb->lock);
+    int64_t s = jb->next;
+    jb->next = s + chunk < jb->total ? s + chunk : jb->total;
+    *end = jb->next;
+    pthread_mutex_unlock(&jb->lock);
+    return s;
+}
+
+/* Row pass for query row i of one head: P_i, D_i, dQ_i, and m_i, l_i. */
+static void bwd_row(const bwd_job_t *jb, int64_t head, int64_t i, double *p,
+                    double *dp)
+{
+    const int64_t nq = jb->nq, nk = jb->nk, d = jb->d;
+    const double *qi = jb->q + (head * nq + i) * d;
+    const double *gi = jb->dout + (head * nq + i) * d;
+    const double *kh = jb->k + head * nk * d;
+    const double *vh = jb->v + head * nk * d;
+    double m, l;
+    probs_row(qi, kh, nk, d, jb->scale, jb->causal, i, p, &m, &l);
+    const int64_t jend = (jb->causal && i + 1 < nk) ? i + 1 : nk;
+    /* dP_ij = dO_i . V_j and D_i = sum_j P_ij dP_ij */
+    double di = 0.0;
+    for (int64_t j = 0; j < jend; ++j) {
+        const double *vj = vh + j * d;
+        double s = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            s += gi[c] * vj[c];
+        dp[j] = s;
+        di += p[j] * s;
+    }
+    /* dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j */
+    double *dqi = jb->dq + (head * nq + i) * d;
+    for (int64_t c = 0; c < d; ++c)
+        dqi[c] = 0.0;
+    for (int64_t j = 0; j < jend; ++j) {
+        const double ds = p[j] * (dp[j] - di);
+        const double *kj = kh + j * d;
+        for (int64_t c = 0; c < d; ++c)
+            dqi[c] += ds * kj[c];
+    }
+    for (int64_t c = 0; c < d; ++c)
+        dqi[c] *= jb->scale;
+    jb->delta[head * nq + i] = di;
+    jb->m[head * nq + i] = m;
+    jb->l[head * nq + i] = l;
+}
+
+/* Key pass for key j of one head: dK_j and dV_j. */
+static void bwd_key(const bwd_job_t *jb, int64_t head, int64_t j)
+{
+    const int64_t nq = jb->nq, nk = jb->nk, d = jb->d;
+    const double *kj = jb->k + (head * nk + j) * d;
+    const double *vj = jb->v + (head * nk + j) * d;
+    double *dkj = jb->dk + (head * nk + j) * d;
+    double *dvj = jb->dv + (head * nk + j) * d;
+    for (int64_t c = 0; c < d; ++c) {
+        dkj[c] = 0.0;
+        dvj[c] = 0.0;
+    }
+    /* causal: key j is visible from the rows i >= j */
+    for (int64_t i = jb->causal ? j : 0; i < nq; ++i) {
+        const double li = jb->l[head * nq + i];
+        if (!(li > 0.0))
+            continue; /* a row with no visible key has P = 0 */
+        const double *qi = jb->q + (head * nq + i) * d;
+        const double *gi = jb->dout + (head * nq + i) * d;
+        /* P_ij exactly as the row pass formed it */
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += qi[c] * kj[c];
+        double pij = jb->scale * dot;
+        pij = exp(pij - jb->m[head * nq + i]);
+        pij /= li;
+        double dpij = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dpij += gi[c] * vj[c];
+        const double ds = pij * (dpij - jb->delta[head * nq + i]);
+        for (int64_t c = 0; c < d; ++c) {
+            dkj[c] += ds * qi[c];
+            dvj[c] += pij * gi[c];
+        }
+    }
+    for (int64_t c = 0; c < d; ++c)
+        dkj[c] *= jb->scale;
+}
 
 static void *bwd_worker(void *arg)
 {
     bwd_job_t *jb = (bwd_job_t *)arg;
-    const int64_t nk = jb->nk, d = jb->d;
-    double *p = (double *)malloc(sizeof(double) * (size_t)nk);
-    double *dp = (double *)malloc(sizeof(double) * (size_t)nk);
-    if (!p || !dp) {
-        free(p);
-        free(dp);
-        jb->failed = 1;
-        return NULL;
+    const int64_t nk = jb->nk;
+    double *p = NULL, *dp = NULL;
+    if (!jb->keys) {
+        p = (double *)malloc(sizeof(double) * (size_t)nk);
+        dp = (double *)malloc(sizeof(double) * (size_t)nk);
+        if (!p || !dp) {
+            free(p);
+            free(dp);
+            pthread_mutex_lock(&jb->lock);
+            jb->failed = 1;
+            pthread_mutex_unlock(&jb->lock);
+            return NULL;
+        }
     }
-    memset(jb->dk_part, 0, sizeof(double) * (size_t)(nk * d));
-    memset(jb->dv_part, 0, sizeof(double) * (size_t)(nk * d));
-    for (int64_t i = jb->r0; i < jb->r1; ++i) {
-        const double *qi = jb->q + i * d;
-        const double *gi = jb->dout + i * d;
-        double m, l;
-        probs_row(qi, jb->k, nk, d, jb->scale, jb->causal, i, p, &m, &l);
-        /* dP_ij and D_i */
-        double di = 0.0;
-        for (int64_t j = 0; j < nk; ++j) {
-            const double *vj = jb->v + j * d;
-            double s = 0.0;
-            for (int64_t c = 0; c < d; ++c)
-                s += gi[c] * vj[c];
-            dp[j] = s;
-            di += p[j] * s;
+    for (;;) {
+        int64_t end;
+        int64_t s = bwd_claim(jb, 16, &end);
+        if (s >= end)
+            break;
+        for (int64_t r = s; r < end; ++r) {
+            if (jb->keys)
+                bwd_key(jb, r / nk, r % nk);
+            else
+                bwd_row(jb, r / jb->nq, r % jb->nq, p, dp);
         }
-        if (jb->delta)
-            jb->delta[i] = di;
-        double *dqi = jb->dq + i * d;
-        for (int64_t c = 0; c < d; ++c)
-            dqi[c] = 0.0;
-        for (int64_t j = 0; j < nk; ++j) {
-            const double ds = p[j] * (dp[j] - di);
-            const double *kj = jb->k + j * d;
-            double *dkj = jb->dk_part + j * d;
-            double *dvj = jb->dv_part + j * d;
-            for (int64_t c = 0; c < d; ++c) {
-                dqi[c] += ds * kj[c];
-                dkj[c] += ds * qi[c];
-                dvj[c] += p[j] * gi[c];
-            }
-        }
-        for (int64_t c = 0; c < d; ++c)
-            dqi[c] *= jb->scale;
     }
     free(p);
     free(dp);
     return NULL;
+}
+
+static int bwd_run(bwd_job_t *jb, int nthreads)
+{
+    if (nthreads > jb->total && jb->total > 0)
+        nthreads = (int)jb->total;
+    if (nthreads < 1)
+        nthreads = 1;
+    pthread_mutex_init(&jb->lock, NULL);
+    jb->next = 0;
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!th) {
+        pthread_mutex_destroy(&jb->lock);
+        return -1;
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&th[started], NULL, bwd_worker, jb) == 0)
+            ++started;
+    bwd_worker(jb); /* the calling thread works too */
+    for (int t = 0; t < started; ++t)
+        pthread_join(th[t], NULL);
+    free(th);
+    pthread_mutex_destroy(&jb->lock);
+    return jb->failed ? -1 : started + 1;
 }
 
 /*
@@ -375,65 +478,32 @@ int oracle_attention_bwd_f64(const double *q, const double *k, const double *v,
         return -1;
     if (nthreads <= 0)
         nthreads = oracle_default_threads();
-    if (nthreads > nq)
-        nthreads = (int)nq;
-    const size_t part = (size_t)(nk * d);
-    double *parts = (double *)malloc(sizeof(double) * part * 2 * (size_t)nthreads);
-    bwd_job_t *jobs = (bwd_job_t *)calloc((size_t)nthreads, sizeof(bwd_job_t));
-    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
-    int *started = (int *)calloc((size_t)nthreads, sizeof(int));
-    int rc = nthreads;
-    if (!parts || !jobs || !th || !started) {
-        rc = -1;
-        goto out;
+    const size_t rows = (size_t)(nh * nq);
+    double *stats = (double *)malloc(sizeof(double) * (rows ? rows : 1) * 3);
+    if (!stats)
+        return -1;
+    bwd_job_t jb;
+    memset(&jb, 0, sizeof(jb));
+    jb.q = q; jb.k = k; jb.v = v; jb.dout = dout;
+    jb.dq = dq; jb.dk = dk; jb.dv = dv;
+    jb.delta = stats;
+    jb.m = stats + rows;
+    jb.l = stats + 2 * rows;
+    jb.nq = nq; jb.nk = nk; jb.d = d;
+    jb.scale = scale;
+    jb.causal = causal;
+    jb.keys = 0;
+    jb.total = nh * nq;
+    int rc = bwd_run(&jb, nthreads);
+    if (rc > 0) {
+        jb.keys = 1;
+        jb.total = nh * nk;
+        jb.failed = 0;
+        int rc2 = bwd_run(&jb, nthreads);
+        rc = rc2 < 0 ? -1 : (rc2 > rc ? rc2 : rc);
     }
-    for (int64_t h = 0; h < nh && rc > 0; ++h) {
-        for (int t = 0; t < nthreads; ++t) {
-            bwd_job_t *jb = &jobs[t];
-            jb->q = q + h * nq * d;
-            jb->dout = dout + h * nq * d;
-            jb->k = k + h * nk * d;
-            jb->v = v + h * nk * d;
-            jb->dq = dq + h * nq * d;
-            jb->delta = delta ? delta + h * nq : NULL;
-            jb->dk_part = parts + (size_t)(2 * t) * part;
-            jb->dv_part = parts + (size_t)(2 * t + 1) * part;
-            jb->r0 = nq * t / nthreads;
-            jb->r1 = nq * (t + 1) / nthreads;
-            jb->nk = nk;
-            jb->d = d;
-            jb->scale = scale;
-            jb->causal = causal;
-            jb->failed = 0;
-            started[t] = 0;
-        }
-        for (int t = 1; t < nthreads; ++t)
-            started[t] = pthread_create(&th[t], NULL, bwd_worker, &jobs[t]) == 0;
-        bwd_worker(&jobs[0]);
-        for (int t = 1; t < nthreads; ++t) {
-            if (started[t])
-                pthread_join(th[t], NULL);
-            else
-                bwd_worker(&jobs[t]); /* could not start: run it here */
-        }
-        double *dkh = dk + h * nk * d, *dvh = dv + h * nk * d;
-        for (size_t e = 0; e < part; ++e) {
-            double sk = 0.0, sv = 0.0;
-            for (int t = 0; t < nthreads; ++t) {
-                sk += parts[(size_t)(2 * t) * part + e];
-                sv += parts[(size_t)(2 * t + 1) * part + e];
-            }
-            dkh[e] = scale * sk;
-            dvh[e] = sv;
-        }
-        for (int t = 0; t < nthreads; ++t)
-            if (jobs[t].failed)
-                rc = -1;
-    }
-out:
-    free(parts);
-    free(jobs);
-    free(th);
-    free(started);
+    if (rc > 0 && delta)
+        memcpy(delta, stats, sizeof(double) * rows);
+    free(stats);
     return rc;
 }

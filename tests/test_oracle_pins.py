@@ -30,9 +30,8 @@ def test_thread_count_does_not_change_bits(orc):
 
 
 def test_bwd_threads_repeatable(orc):
-    """The gradient oracle gives the same bits for the same thread count, and
-    agrees to rounding across thread counts (only the order in which the
-    per-thread dK/dV partial sums are added changes)."""
+    """The gradient oracle gives the same bits whatever the thread count: no
+    sum is split between threads."""
     r = np.random.default_rng(5)
     q, k, v, g = (r.standard_normal((2, 77, 16)) for _ in range(4))
     a = orc.attention_bwd(q, k, v, g, 0.3, True, nthreads=3)
@@ -40,7 +39,7 @@ def test_bwd_threads_repeatable(orc):
     c = orc.attention_bwd(q, k, v, g, 0.3, True, nthreads=1)
     for i in range(4):
         assert np.array_equal(a[i], b[i])
-        assert np.allclose(a[i], c[i], rtol=0, atol=1e-13)
+        assert np.array_equal(a[i], c[i])
     assert a[4] == 3 and c[4] == 1
 
 
