@@ -409,6 +409,45 @@ def pin_fp8_quantize_error(orc):
            tol=1e-6, what="rotation inner products")
 
 
+def pin_fp8_block_grouping(orc):
+    """Which rows share a scale.  Blocks are runs of ``block_rows``
+    consecutive rows of one head, the last one possibly short.  A value
+    planted in row r of one head, far above every other magnitude, must move
+    exactly block r // R of that head, to the closed-form exponent of the
+    planted value (1000: 448 * 2^1 < 1000 <= 448 * 2^2, so e = 2), and leave
+    every other block of every head with its codes and exponent unchanged --
+    with and without the rotation (which spreads the value over its row, so
+    the block maximum stays within 1000 +- 0.64 here).  And every block uses
+    the top of the e4m3 range: its largest code magnitude is at least 224
+    (the block maximum scaled into (224, 448], then rounded)."""
+    import oracle as orc_mod
+    r = _rng(43)
+    n, d = 200, 64
+    x = (r.uniform(-0.01, 0.01, (2, 3, n, d))).astype(np.float32)
+    signs = r.choice([-1.0, 1.0], d)
+    for sg in (None, signs):
+        for R in (64, 128):
+            nb = -(-n // R)
+            c0, e0 = orc_mod.quantize_fp8(x, R, sg)
+            assert e0.shape == (2, 3, nb), e0.shape
+            vals = np.abs(orc_mod.e4m3_values(c0))
+            for b in range(nb):
+                top = vals[..., b * R:min(n, (b + 1) * R), :].max(axis=(-2, -1))
+                assert np.all(top >= 224), (R, b, top)
+            for (bi, hi, row) in ((0, 0, 0), (1, 2, R - 1), (0, 1, R),
+                                  (1, 0, n - 1), (0, 2, 131)):
+                xp = x.copy()
+                xp[bi, hi, row, 5] = 1000.0
+                c1, e1 = orc_mod.quantize_fp8(xp, R, sg)
+                blk = row // R
+                assert e1[bi, hi, blk] == 2, (R, row, e1[bi, hi, blk])
+                moved = np.argwhere(e1 != e0)
+                assert [tuple(m) for m in moved] == [(bi, hi, blk)], (R, row, moved)
+                same = np.ones(c0.shape, dtype=bool)
+                same[bi, hi, blk * R:min(n, (blk + 1) * R)] = False
+                assert np.array_equal(c1[same], c0[same]), (R, row)
+
+
 # ---------------------------------------------------------------------------
 # gradients
 
@@ -599,6 +638,7 @@ ALL_PINS = [
     pin_e4m3_codes,
     pin_block_exponent,
     pin_fp8_quantize_error,
+    pin_fp8_block_grouping,
     pin_bwd_finite_differences,
     pin_gqa_bwd_finite_differences,
     pin_bwd_sums,
