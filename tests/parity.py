@@ -3,10 +3,13 @@
 Tolerances (bf16 inputs; the benchmark spec's max-abs 1e-2 and rel-L2 5e-3):
 * fp32 output (fa2_fwd_o32): max |O - O_ref| <= 1e-2 and
   ||O - O_ref||_2 / ||O_ref||_2 <= 5e-3, literally;
-* bf16 output (fa2_fwd): the stored value is O rounded to bf16, whose own
-  rounding is up to half a bf16 ulp (1.6e-2 for 4 <= |O| < 8), so each
+* bf16 output (fa2_fwd): max |O - O_ref| <= 1e-2 literally (``literal=True``)
+  wherever the outputs stay below 4 in magnitude, which holds for standard
+  normal inputs (the training, causal and long-sequence workloads); where
+  they do not (the x20 outlier workload reaches |O| > 5) the stored value's
+  own rounding is up to half a bf16 ulp (1.6e-2 for 4 <= |O| < 8), so each
   element must satisfy |O - O_ref| <= max(1e-2, ulp_bf16(O_ref)); rel-L2 as
-  above; the literal max-abs is reported alongside;
+  above in both cases; the literal max-abs is reported alongside;
 * lse: |lse - lse_ref| <= 1e-3 + 2e-6 |lse_ref|.
 fp32 inputs (fa2_fwd_fp32): max-abs <= 1e-5 on O and lse.
 
@@ -124,11 +127,13 @@ def rounding_bound(o_ref, v, heads, out_kind="bf16"):
     return np.broadcast_to(e, o_ref.shape)
 
 
-def compare(o, o_ref, lse=None, lse_ref=None, out_kind="bf16", elem_bound=None):
+def compare(o, o_ref, lse=None, lse_ref=None, out_kind="bf16", elem_bound=None,
+            literal=False):
     """Return a dict of error figures and booleans; ``out_kind`` is "bf16",
     "fp32" (bf16 inputs, fp32 output) or "fp32in" (fp32 everything).
     ``elem_bound`` (bf16 inputs only), if given, widens the element-wise
-    bound to max(stated bound, elem_bound) (see :func:`rounding_bound`)."""
+    bound to max(stated bound, elem_bound) (see :func:`rounding_bound`).
+    ``literal`` holds a bf16 output to max-abs 1e-2 exactly (no ulp term)."""
     o = np.asarray(o, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
     assert o.shape == o_ref.shape, (o.shape, o_ref.shape)
@@ -145,7 +150,7 @@ def compare(o, o_ref, lse=None, lse_ref=None, out_kind="bf16", elem_bound=None):
         res["worst_over_bound"] = worst
         res["o_ok"] = finite and worst <= 1.0 and rel_l2 <= REL_L2
     else:
-        bound = np.maximum(MAX_ABS, ulp_bf16(o_ref))
+        bound = MAX_ABS if literal else np.maximum(MAX_ABS, ulp_bf16(o_ref))
         if elem_bound is not None:
             bound = np.maximum(bound, elem_bound)
         worst = float((err / bound).max()) if err.size else 0.0

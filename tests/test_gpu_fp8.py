@@ -114,10 +114,15 @@ def test_fp8_end_to_end(fa2):
     assert plain["rel_l2"] > 2.0 * rot["rel_l2"], (plain, rot)
 
 
+@pytest.mark.timeout(600)
 def test_fp8_full_size_headline(fa2):
     """The headline shape (B=2, H=16, N=8192, d=128, causal) with rotation:
-    sampled rows of two heads against the exact attention of the
-    dequantised inputs, every output finite."""
+    every element of every head against the exact attention of the
+    dequantised inputs (rel-L2 and max-abs relative to the largest
+    reference value, over the whole tensor and within each head), every
+    output finite."""
+    import time
+
     import torch  # noqa: F811
     w = wl.WORKLOADS[wl.HEADLINE]
     q, k, v = wl.workload_inputs(w)
@@ -125,17 +130,17 @@ def test_fp8_full_size_headline(fa2):
     say("fp8 full size %s" % w.describe())
     o, lse = run_fp8(fa2, q, k, v, True, signs)
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(w.N - 8, w.N),
-                                     rng.choice(w.N, 48, replace=False)])).astype(np.int64)
-    sg = signs.numpy()
-    for b, h in ((0, 0), (1, 15)):
-        q8, qe = oracle.quantize_fp8(q[b, h], 128, sg)
-        k8, ke = oracle.quantize_fp8(k[b, h], 64, sg)
-        v8, ve = oracle.quantize_fp8(v[b, h], 64, None)
-        qd = oracle.dequantize_fp8(q8, qe, 128)
-        kd = oracle.dequantize_fp8(k8, ke, 64)
-        vd = oracle.dequantize_fp8(v8, ve, 64)
-        o_ref, _, _ = oracle.attention_rows(qd[rows], rows, kd, vd, w.scale / w.d, True)
-        res = parity.compare_fp8(parity.to_np(o[b, h][rows]), o_ref)
-        assert res["rel_l2"] <= parity.FP8_REL_L2 and res["max_rel"] <= parity.FP8_MAX_REL, res
+    say("fp8 oracle (all heads)")
+    t0 = time.time()
+    o_ref, _, _ = oracle.attention_fp8_reference(q, k, v, w.scale, True,
+                                                 signs=signs.numpy())
+    say("fp8 oracle done in %.1f s" % (time.time() - t0))
+    on = parity.to_np(o)
+    res = parity.compare_fp8(on, o_ref)
+    say("  whole tensor: " + parity.describe(res))
+    assert res["rel_l2"] <= parity.FP8_REL_L2 and res["max_rel"] <= parity.FP8_MAX_REL, res
+    oh = on.reshape(w.B * w.H, w.N, w.d)
+    rh = o_ref.reshape(w.B * w.H, w.N, w.d)
+    for h in range(w.B * w.H):
+        rs = parity.compare_fp8(oh[h], rh[h])
+        assert rs["rel_l2"] <= parity.FP8_REL_L2 and rs["max_rel"] <= parity.FP8_MAX_REL, (h, rs)

@@ -116,52 +116,45 @@ def test_scale_values(fa2, scale):
         assert res["ok"], parity.describe(res)
 
 
-def sample_rows(N, rng, extra=24):
-    rows = set(range(min(8, N))) | set(range(max(0, N - 8), N))
-    for b in (127, 128, 129, N // 2, N // 2 + 1):
-        if 0 <= b < N:
-            rows.add(b)
-    rows |= set(int(x) for x in rng.choice(N, size=min(extra, N), replace=False))
-    return np.array(sorted(rows), dtype=np.int64)
-
-
 BIG = [n for n, w in wl.WORKLOADS.items()
        if w.dtype == "bf16" and w.q_rows == w.N]
 
 
+def full_oracle(w, q, k, v):
+    """The fp64 oracle over every head of a workload (grouped K/V heads
+    expanded by their definition)."""
+    if w.kv_heads != w.H:
+        return oracle.attention_gqa(q, k, v, w.scale, w.causal)[:2]
+    return oracle.attention(q, k, v, w.scale, w.causal)[:2]
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", BIG)
 def test_full_size_workload(fa2, name):
     """Each bf16 workload at its full size, in the launch configuration the
-    benchmark uses: every output finite and written, and sampled rows of
-    three heads (first, middle, last) against the oracle row by row."""
+    benchmark uses, compared with the fp64 oracle element by element over
+    the whole output (every head, every row), for both output types;
+    rel-L2 is taken over the whole tensor.  A bf16 output is held to the
+    literal max-abs 1e-2 except on the x20 outlier workload, whose outputs
+    exceed 4 in magnitude, where half a bf16 spacing of the stored value
+    alone can exceed it (bound max(1e-2, ulp_bf16(O_ref)))."""
+    import time
+
     import torch
     w = wl.WORKLOADS[name]
     q, k, v = wl.workload_inputs(w)
-    BH = w.B * w.H
-    rng = np.random.default_rng(5)
-    heads = sorted({0, BH // 2, BH - 1})
-    rows = sample_rows(w.N, rng)
-    kx, vx = k, v
-    if w.kv_heads != w.H:  # grouped K/V heads, by their definition
-        kx = oracle.expand_kv_heads(k, w.H)
-        vx = oracle.expand_kv_heads(v, w.H)
-    qf, kf, vf = (t.reshape(BH, w.N, w.d) for t in (q, kx, vx))
-    refs = {}
-    for h in heads:
-        refs[h] = oracle.attention_rows(qf[h, rows], rows, kf[h], vf[h],
-                                        w.scale, w.causal)
+    say("oracle %s (all heads)" % w.describe())
+    t0 = time.time()
+    o_ref, l_ref = full_oracle(w, q, k, v)
+    say("oracle done in %.1f s" % (time.time() - t0))
     for odt, kind in ((torch.bfloat16, "bf16"), (torch.float32, "fp32")):
         say("workload %s out=%s" % (w.describe(), kind))
         o, lse = run(fa2, q, k, v, w.causal, out_dtype=odt)
-        assert torch.isfinite(o).all(), "non-finite or unwritten output"
-        assert torch.isfinite(lse).all(), "non-finite or unwritten lse"
-        of = o.reshape(BH, w.N, w.d)
-        lf = lse.reshape(BH, w.N)
-        for h in heads:
-            o_ref, l_ref, _ = refs[h]
-            res = parity.compare(parity.to_np(of[h, rows]), o_ref,
-                                 parity.to_np(lf[h, rows]), l_ref, kind)
-            assert res["ok"], "head %d: %s" % (h, parity.describe(res))
+        res = parity.compare(parity.to_np(o), o_ref, parity.to_np(lse), l_ref,
+                             kind, literal=not w.outliers)
+        say("  " + parity.describe(res))
+        assert res["ok"], parity.describe(res)
+        del o, lse
 
 
 def test_deterministic(fa2):
