@@ -115,6 +115,84 @@ def read_traffic(workload_name: str, which: str = "fwd"):
     return fetch + write
 
 
+def rocm_version() -> str:
+    """ROCm release of the installation (``/opt/rocm/.info/version``)."""
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            return f.read().strip()
+    except OSError:
+        return "unknown"
+
+
+class ClockSampler:
+    """Engine (GFX) clock of the benchmarked GPU read through amdsmi while
+    the timed kernels run: the power limit lowers the clock under load, so
+    the achieved fraction of the 2.4 GHz peak mixes kernel efficiency with
+    the clock.  Every failure leaves the sampler disabled (``None`` in the
+    record); it never affects the timing itself."""
+
+    def __init__(self, torch, dev):
+        self.samples = []
+        self.source = None
+        self._read = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            handle = handles[0] if len(handles) == 1 else None
+            try:  # match the torch device by PCI address
+                props = torch.cuda.get_device_properties(dev)
+                want = "%04x:%02x:%02x" % (props.pci_domain_id, props.pci_bus_id,
+                                           props.pci_device_id)
+                for h in handles:
+                    if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
+                        handle = h
+            except Exception:
+                pass
+            if handle is None:
+                return
+
+            def read_metrics():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                val = m.get("current_gfxclk", m.get("average_gfxclk_frequency"))
+                if isinstance(val, (list, tuple)):
+                    val = max(x for x in val if isinstance(x, (int, float)))
+                return float(val)
+
+            def read_clock():
+                return float(amdsmi.amdsmi_get_clock_info(
+                    handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+
+            for fn, name in ((read_metrics, "amdsmi gpu metrics, current gfxclk"),
+                             (read_clock, "amdsmi clock info, GFX")):
+                try:
+                    v = fn()
+                    if 100.0 <= v <= 5000.0:
+                        self._read, self.source = fn, name
+                        break
+                except Exception:
+                    continue
+        except Exception:
+            self._read = None
+
+    def poll_until(self, event, period_s=0.002):
+        """Sample until ``event`` has completed (the timed kernels drained)."""
+        while not event.query():
+            if self._read is not None:
+                try:
+                    self.samples.append(self._read())
+                except Exception:
+                    self._read = None
+            time.sleep(period_s)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        s = sorted(self.samples)
+        return {"mean_mhz": round(sum(s) / len(s), 1), "min_mhz": s[0],
+                "max_mhz": s[-1], "samples": len(s), "source": self.source}
+
+
 def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
     """Time the fp64 gradient oracle (as it stands) on whole heads of the
     workload, as many as fit the budget after timing the first one."""
@@ -342,6 +420,7 @@ def main(argv=None):
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
+    clock = ClockSampler(torch, dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     start = torch.cuda.Event(enable_timing=True)
@@ -350,6 +429,7 @@ def main(argv=None):
     for _ in range(args.steps):
         step()
     end.record(stream)
+    clock.poll_until(end)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
@@ -413,6 +493,10 @@ def main(argv=None):
         "compulsory_hbm_bytes": comp,
         "kernel_source_sha256": kernel_source_hash("fp8" if fp8 else args.which),
         "gpu": torch.cuda.get_device_name(dev),
+        "gfx_clock_during_timed_steps": clock.summary(),
+        "rocm": rocm_version(),
+        "torch": torch.__version__,
+        "seed": wl.DEFAULT_SEED,
     }
     if per_call is not None:
         rec["per_call"] = per_call
