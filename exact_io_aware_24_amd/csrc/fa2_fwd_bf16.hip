@@ -10,9 +10,10 @@
 //     if mt > m + 8 for any row of the wave:   (lazy rescale, see below)
 //         a = 2^(m - max(m, mt)); m = max(m, mt); l *= a; O~ *= a
 //     P~ = 2^(S*c - m)                    fp32, hardware exp2
-//     l  = l + rowsum(P~)
-//     O~ = O~ + P~ . V_tile               P~ rounded to bf16, MFMA, fp32 acc
-//   and after the last tile O = O~ / l, lse = (m + log2 l) * ln 2.
+//     l  = l + rowsum(P~)                 (for the lse)
+//     lb = lb + rowsum(bf16(P~))          (the normaliser of O~)
+//     O~ = O~ + bf16(P~) . V_tile         MFMA, fp32 acc
+//   and after the last tile O = O~ / lb, lse = (m + log2 l) * ln 2.
 // The running (m, l, O~) update is the two-block online-softmax merge of the
 // shakilmahmud.com page "Large language models part 06: FlashAttention --
 // GPU SRAM, tiling, online softmax", section 2, with O~ kept unnormalised so
@@ -26,6 +27,14 @@
 // reference is therefore raised only when a tile's maximum exceeds it by more
 // than 8 (a factor 256), which keeps every P~ <= 2^8 (no overflow, the same
 // relative bf16 precision) and skips the O~ rescale on most tiles.
+//
+// Normaliser: O~ is divided by the sum of the bf16-rounded P~ that multiplied
+// V (v_dot2 of each rounded pair against (1, 1)), so the weights applied to
+// V sum to one exactly.  Dividing by the sum of the unrounded values instead
+// leaves the rounding of a dominant P~ -- anywhere in (1, 2^8] under the lazy
+// rescale, not exactly 1 -- in O undiluted, up to 2^-8 of |V|, which exceeds
+// the stated tolerance on sharp softmaxes (the x20 outlier rows).  The lse
+// keeps the fp32 sum of the unrounded values.
 //
 // gfx950 mapping (this library's design, not the pages'):
 //  * 256 threads = 4 wave64s; wave w owns query rows [32w, 32w+32) of the
@@ -130,6 +139,7 @@ struct WaveState {
   f32x16 oacc[Cfg<D>::NCT];
   float m_run;  // reference max (base-2 scaled units)
   float l_run;  // this half-wave's share of the running sum
+  float lr_run; // the same for the bf16-rounded P~ (the normaliser of O~)
 };
 
 // Per-thread byte offsets fixed for the whole kernel.
@@ -248,6 +258,7 @@ __device__ __forceinline__ void softmax_max(f32x16 (&s)[Cfg<D>::NKT],
         (m_new == -INFINITY) ? 1.f : fast_exp2(st.m_run - m_new);
     st.m_run = m_new;
     st.l_run *= alpha;
+    st.lr_run *= alpha;
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
@@ -264,7 +275,7 @@ template <int D, bool MASKED>
 __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[Cfg<D>::NKT],
                                             float mu, float c,
                                             bf16x8 (&pb)[Cfg<D>::NKT][2],
-                                            float &l_run) {
+                                            float &l_run, float &lr_run) {
   using C = Cfg<D>;
   float rs = 0.f;
 #pragma unroll
@@ -280,6 +291,19 @@ __device__ __forceinline__ void softmax_exp(const f32x16 (&s)[Cfg<D>::NKT],
         pb[kt][u][e] = static_cast<__bf16>(x);
       }
   l_run += rs;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  float rr = lr_run;
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pb[kt][u][e], pb[kt][u][e + 1]};
+        rr = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rr, false);
+      }
+  lr_run = rr;
 }
 
 // O^T += V^T P^T: A operand = columns 32ct + lane%32 of the keys above,
@@ -450,6 +474,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       for (int r2 = 0; r2 < 16; ++r2) st.oacc[ct][r2] = 0.f;
     st.m_run = -INFINITY;
     st.l_run = 0.f;
+    st.lr_run = 0.f;
 
     // ---- tile schedule -----------------------------------------------------
     // Software pipeline: iteration t computes the scores of tile t+1 (K one
@@ -509,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       issue_v<D>(vh, head_bytes, off, vbuf(1 - P), wv, (j0 + C::BC) * D * 2);
       scores<D>(kbuf(1 - P), off, st.qreg, nxt);
       bf16x8 pb[C::NKT][2];
-      softmax_exp<D, false>(cur, st.m_run, c, pb, st.l_run);
+      softmax_exp<D, false>(cur, st.m_run, c, pb, st.l_run, st.lr_run);
       pv<D>(vbuf(P), off, pb, st.oacc);
       softmax_max<D, CAUSAL, false>(nxt, st, c, j0 + C::BC, Nk, qpos, hh);
       __builtin_amdgcn_s_waitcnt(0);
@@ -559,7 +584,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       if (t < w_tiles) {
         const float mu = (st.m_run == -INFINITY) ? 0.f : st.m_run;
         bf16x8 pb[C::NKT][2];
-        softmax_exp<D, true>(sa, mu, c, pb, st.l_run);
+        softmax_exp<D, true>(sa, mu, c, pb, st.l_run, st.lr_run);
         pv<D>(vbuf(pr), off, pb, st.oacc);
       }
       if (t + 1 < w_tiles)
@@ -577,12 +602,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     }  // tb < ntiles
 
     // ---- epilogue: O = O~ / l, lse -------------------------------------------
-    float llo, lhi;
+    float llo, lhi, rlo, rhi;
     halves(st.l_run, llo, lhi);
+    halves(st.lr_run, rlo, rhi);
     const float l_tot = llo + lhi;
+    const float lr_tot = rlo + rhi;
     // a row that saw no key (only possible within one key range of a split,
     // or causal with more queries than keys): O = 0, lse = -inf
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
     if (qi < Nq) {
       const size_t head = qhead + split * p.o_split_stride;
       // O^T register r of row tile ct holds column 32ct + 8(r/4) + 4hh + r%4
