@@ -28,10 +28,13 @@ FA2_ERR_SCALE = -4
 FA2_ERR_ALIGN = -5
 FA2_ERR_ALIAS = -6
 FA2_ERR_HIP = -7
+FA2_ERR_WORKSPACE = -8
+NOALLOC_WORKSPACE_BYTES = 32 << 20  # FA2_NOALLOC_WORKSPACE_BYTES
 
 # Every symbol include/fa2.h declares.
 EXPORTED = ("fa2_fwd", "fa2_fwd_o32", "fa2_fwd_gqa", "fa2_fwd_gqa_o32",
-            "fa2_fwd_splitkv", "fa2_fwd_splitkv_o32", "fa2_quantize_fp8",
+            "fa2_fwd_splitkv", "fa2_fwd_splitkv_o32", "fa2_fwd_splitkv_noalloc",
+            "fa2_quantize_fp8",
             "fa2_fwd_fp8", "fa2_fwd_fp8_o32", "fa2_fwd_fp32", "fa2_bwd",
             "fa2_bwd_o32", "fa2_bwd_gqa", "fa2_bwd_gqa_o32", "fa2_strerror",
             "fa2_version")
@@ -76,6 +79,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = ssig
             f.restype = ctypes.c_int
+        L.fa2_fwd_splitkv_noalloc.argtypes = [vp] * 5 + [i] * 6 + [ctypes.c_float, i, i, vp]
+        L.fa2_fwd_splitkv_noalloc.restype = ctypes.c_int
         L.fa2_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp]
         L.fa2_quantize_fp8.restype = ctypes.c_int
         for name in ("fa2_fwd_fp8", "fa2_fwd_fp8_o32"):
@@ -363,6 +368,45 @@ def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
             int(n_splits), ptr(o_part), ptr(lse_part), stream)
     if rc != FA2_OK:
         raise FA2Error(rc, fn)
+    return out, lse
+
+
+def forward_splitkv_noalloc(q, k, v, causal: bool = False,
+                            scale: float | None = None, n_splits: int | None = None,
+                            out=None, lse=None, return_lse: bool = True):
+    """``fa2_fwd_splitkv_noalloc``: :func:`forward_splitkv` (bf16 output)
+    with the key-range partials in the library's static device workspace.
+    ``out`` and ``lse`` are allocated here when not given (torch memory);
+    pass them to keep the call allocation-free.  Returns ``(o, lse)``."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4 or not t.is_cuda \
+                or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("%s must be a contiguous bfloat16 GPU tensor [B, H, N, d]" % name)
+    B, H, Nq, d = (int(x) for x in q.shape)
+    H_kv, Nk = int(k.shape[1]), int(k.shape[2])
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d or H_kv < 1 \
+            or H % H_kv != 0 or not (q.device == k.device == v.device):
+        raise ValueError("k, v must be [B, H_kv, Nk, d] with H_kv dividing H")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_splits is None:
+        n_splits = default_splits(B, H, Nq, Nk, d)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = lib().fa2_fwd_splitkv_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, B, H, H_kv, Nq, Nk, d,
+            ctypes.c_float(scale), int(bool(causal)), int(n_splits), stream)
+    if rc != FA2_OK:
+        raise FA2Error(rc, "fa2_fwd_splitkv_noalloc")
     return out, lse
 
 

@@ -8,6 +8,9 @@
 
 #include "fa2_internal.h"
 
+static_assert(fa2::kFwdScratchBytes == FA2_NOALLOC_WORKSPACE_BYTES,
+              "the header states the static workspace size");
+
 #define FA2_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
@@ -263,6 +266,41 @@ FA2_EXPORT int fa2_fwd_splitkv_o32(const void *q, const void *k, const void *v,
                  n_splits, o_part, lse_part, true, stream);
 }
 
+// fa2_fwd_splitkv with the partial (O, lse) of the key ranges in the
+// library's static per-device workspace instead of caller memory: no
+// allocation anywhere on this path.  Every element of the partials that the
+// merge reads is written by the range kernel of the same call first, so the
+// workspace needs no clearing (it keeps the previous call's values).
+FA2_EXPORT int fa2_fwd_splitkv_noalloc(const void *q, const void *k,
+                                       const void *v, void *o, float *lse,
+                                       int B, int H, int H_kv, int Nq, int Nk,
+                                       int d, float scale, int causal,
+                                       int n_splits, void *stream) {
+  int rc = validate(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, 2, 2,
+                    fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc != FA2_OK) return rc;
+  if (n_splits < 1 || n_splits > FA2_MAX_SPLITS) return FA2_ERR_SHAPE;
+  const int64_t bh = static_cast<int64_t>(B) * H;
+  const int64_t blocks = bh * ((static_cast<int64_t>(Nq) + fa2::kBf16RowsPerBlock - 1) /
+                               fa2::kBf16RowsPerBlock);
+  if (blocks * n_splits > INT32_MAX) return FA2_ERR_SHAPE;
+  fa2::FwdArgs a = make_args(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal);
+  a.n_splits = n_splits;
+  if (n_splits > 1) {
+    // [n_splits][B*H][Nq][d] fp32 partial outputs, then [n_splits][B*H][Nq]
+    // fp32 partial lse (the first part is a multiple of 256 bytes: d >= 64)
+    const int64_t o_floats = static_cast<int64_t>(n_splits) * bh * Nq * d;
+    const int64_t l_floats = static_cast<int64_t>(n_splits) * bh * Nq;
+    if ((o_floats + l_floats) * 4 > static_cast<int64_t>(FA2_NOALLOC_WORKSPACE_BYTES))
+      return FA2_ERR_WORKSPACE;
+    float *ws = nullptr;
+    if (fa2::fwd_scratch(&ws) != hipSuccess) return FA2_ERR_HIP;
+    a.o_part = ws;
+    a.lse_part = ws + o_floats;
+  }
+  return finish(fa2::launch_fwd_bf16(a, false, static_cast<hipStream_t>(stream)));
+}
+
 FA2_EXPORT int fa2_quantize_fp8(const void *x, void *codes, int *exps, int B,
                                 int H, int N, int d, int block_rows,
                                 const float *signs, void *stream) {
@@ -422,8 +460,11 @@ FA2_EXPORT const char *fa2_strerror(int code) {
     case FA2_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FA2_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA2_ERR_HIP: return "HIP kernel launch failed";
+    case FA2_ERR_WORKSPACE:
+      return "the key-range partials exceed the library's static workspace "
+             "(FA2_NOALLOC_WORKSPACE_BYTES)";
     default: return "unknown fa2 error code";
   }
 }
 
-FA2_EXPORT int fa2_version(void) { return 6; }
+FA2_EXPORT int fa2_version(void) { return 7; }

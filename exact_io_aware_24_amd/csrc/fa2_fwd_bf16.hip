@@ -80,6 +80,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "fa2_device.h"
@@ -738,6 +739,31 @@ hipError_t launch_merge(const FwdArgs &a, bool o32, size_t o_stride,
 }
 
 }  // namespace
+
+// Workspace of fa2_fwd_splitkv_noalloc, one copy per device for the life of
+// the process.  Host code never uses the name itself as an address (on the
+// host it is only a stand-in): fwd_scratch() looks the device address up.
+static __device__ __align__(256) float scratch[kFwdScratchBytes / sizeof(float)];
+
+hipError_t fwd_scratch(float **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = static_cast<float *>(addr[dev]);
+  return hipSuccess;
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s) {
   Params prm;

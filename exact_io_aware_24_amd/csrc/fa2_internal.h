@@ -51,6 +51,13 @@ struct BwdArgs {
 // bf16 q/k/v on MFMA; o is bf16 (o32 == false) or fp32 (o32 == true).
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s);
 
+// Bytes of the library's static device workspace (fa2_fwd_splitkv_noalloc:
+// the fp32 partial outputs and lse of the key ranges).
+constexpr size_t kFwdScratchBytes = size_t(32) << 20;
+// Device address of that workspace on the current device (looked up once
+// per device); no allocation.
+hipError_t fwd_scratch(float **ptr);
+
 // Gradients (bf16 MFMA); dq/dk/dv bf16 (o32 == false) or fp32 (true).
 hipError_t launch_bwd_bf16(const BwdArgs &a, bool o32, hipStream_t s);
 

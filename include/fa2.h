@@ -31,7 +31,9 @@
  *
  * Ownership and lifetime: the caller allocates and owns every buffer; the
  * library allocates no device or host memory and keeps no state other than
- * what the HIP runtime caches.  All pointers are device pointers (hipMalloc
+ * what the HIP runtime caches and one static device array per GPU (the
+ * workspace of fa2_fwd_splitkv_noalloc, FA2_NOALLOC_WORKSPACE_BYTES, held
+ * until the process ends).  All pointers are device pointers (hipMalloc
  * or equivalent) of the current HIP device.  Calls are thread-safe.
  *
  * Asynchrony: every entry point enqueues its kernel on `stream` (a
@@ -65,6 +67,8 @@ extern "C" {
 #define FA2_ERR_ALIGN (-5)   /* a pointer is not 16-byte aligned               */
 #define FA2_ERR_ALIAS (-6)   /* an output overlaps an input or another output  */
 #define FA2_ERR_HIP (-7)     /* the kernel launch failed (hipGetLastError)     */
+#define FA2_ERR_WORKSPACE (-8) /* fa2_fwd_splitkv_noalloc: the partials need
+                                  more than FA2_NOALLOC_WORKSPACE_BYTES      */
 
 /* Size limits (FA2_ERR_SHAPE beyond them): B*H*N*d <= FA2_MAX_ELEMS elements
    per tensor (2^40, far above one GPU's memory); B*H and the number of
@@ -76,6 +80,8 @@ extern "C" {
 #define FA2_MAX_HEAD_ELEMS_BF16 ((1LL << 30) - (1LL << 16))
 /* Largest n_splits of fa2_fwd_splitkv. */
 #define FA2_MAX_SPLITS 1024
+/* Size of the static per-device workspace of fa2_fwd_splitkv_noalloc. */
+#define FA2_NOALLOC_WORKSPACE_BYTES (32u << 20)
 
 /*
  * fa2_fwd -- bf16 inputs, bf16 output.
@@ -160,6 +166,28 @@ int fa2_fwd_splitkv_o32(const void *q, const void *k, const void *v, float *o,
                         float *lse, int B, int H, int H_kv, int Nq, int Nk,
                         int d, float scale, int causal, int n_splits,
                         float *o_part, float *lse_part, void *stream);
+
+/*
+ * fa2_fwd_splitkv_noalloc -- fa2_fwd_splitkv (bf16 o) for callers that cannot
+ * allocate memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results
+ * (bit-identical to fa2_fwd_splitkv with the same n_splits), but the fp32
+ * partial outputs and lse of the key ranges live in a static device array
+ * of FA2_NOALLOC_WORKSPACE_BYTES (32 MiB) that the library holds on every
+ * GPU it runs on until the process ends; the call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).  With n_splits > 1 it
+ * needs n_splits * B * H * Nq * (d + 1) * 4 bytes of that array; more is
+ * FA2_ERR_WORKSPACE (checked on the host before any HIP call).  The first
+ * call on a device looks up the array's device address (FA2_ERR_HIP if that
+ * fails).  Every call on one GPU shares that GPU's array and leaves its
+ * values behind; the range kernel writes every partial the merge reads, so
+ * nothing needs clearing.  Calls that overlap in time on one GPU (different
+ * streams, or host threads) race on the array: the caller serialises them.
+ */
+int fa2_fwd_splitkv_noalloc(const void *q, const void *k, const void *v,
+                            void *o, float *lse, int B, int H, int H_kv,
+                            int Nq, int Nk, int d, float scale, int causal,
+                            int n_splits, void *stream);
 
 /*
  * FP8 path: block quantisation with incoherent processing (the FP8 recipe
@@ -288,9 +316,9 @@ int fa2_bwd_gqa_o32(const void *q, const void *k, const void *v,
 /* Static English description of a return code (never NULL). */
 const char *fa2_strerror(int code);
 
-/* Library ABI version: 6 (2 added the backward pass, 3 grouped K/V heads,
+/* Library ABI version: 7 (2 added the backward pass, 3 grouped K/V heads,
    4 split key ranges with separate query and key lengths, 5 the FP8 path,
-   6 the grouped-head backward). */
+   6 the grouped-head backward, 7 fa2_fwd_splitkv_noalloc). */
 int fa2_version(void);
 
 #ifdef __cplusplus

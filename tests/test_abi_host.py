@@ -50,7 +50,7 @@ def test_codes_match_header():
 
 
 def test_version_and_strerror(L):
-    assert fa2.version() == 6
+    assert fa2.version() == 7
     seen = set()
     for name, code in header_codes().items():
         msg = fa2.strerror(code)
@@ -290,6 +290,40 @@ def test_splitkv_validation(L, fn):
         for other in ("q", "k", "v", "o", "lse"):
             assert call_split(fn, {part: SPLIT_GOOD[other] + 16}) == fa2.FA2_ERR_ALIAS, (part, other)
     assert call_split(fn, {"lse_part": SPLIT_GOOD["o_part"] + 64}) == fa2.FA2_ERR_ALIAS
+
+
+def call_noalloc(ptrs=None, B=1, H=4, H_kv=2, Nq=16, Nk=1000, d=128,
+                 scale=0.1, causal=1, n_splits=4):
+    p = dict(SPLIT_GOOD)
+    p.update(ptrs or {})
+    return int(fa2.lib().fa2_fwd_splitkv_noalloc(
+        *[p[n] for n in SPLIT_NAMES[:5]], B, H, H_kv, Nq, Nk, d,
+        ctypes.c_float(scale), causal, n_splits, None))
+
+
+def test_splitkv_noalloc_validation(L):
+    """The allocation-free split-KV entry point validates like
+    fa2_fwd_splitkv, and a problem whose partials exceed the static
+    workspace is refused with FA2_ERR_WORKSPACE on the host, before any HIP
+    call."""
+    for kw in (dict(Nq=0), dict(Nk=0), dict(H_kv=3), dict(n_splits=0),
+               dict(n_splits=fa2.MAX_SPLITS + 1)):
+        assert call_noalloc(**kw) == fa2.FA2_ERR_SHAPE, kw
+    for name in ("q", "k", "v", "o"):
+        assert call_noalloc({name: None}) == fa2.FA2_ERR_NULL, name
+    assert call_noalloc(d=80) == fa2.FA2_ERR_HEADDIM
+    assert call_noalloc(scale=float("nan")) == fa2.FA2_ERR_SCALE
+    assert call_noalloc({"o": SPLIT_GOOD["o"] + 4}) == fa2.FA2_ERR_ALIGN
+    assert call_noalloc({"o": SPLIT_GOOD["q"] + 16}) == fa2.FA2_ERR_ALIAS
+    # n_splits * B * H * Nq * (d + 1) * 4 bytes against the 32 MiB array
+    lim = fa2.NOALLOC_WORKSPACE_BYTES
+    rows_ok = lim // (4 * 129 * 4)          # n_splits = 4, d = 128
+    assert 4 * rows_ok * 129 * 4 <= lim < 4 * (rows_ok + 1) * 129 * 4
+    big = dict(B=1, H=rows_ok + 1, H_kv=1, Nq=1, Nk=1000, n_splits=4)
+    assert call_noalloc(**big) == fa2.FA2_ERR_WORKSPACE
+    assert call_noalloc(B=1, H=1, H_kv=1, Nq=1 << 16, Nk=1 << 16,
+                        n_splits=2) == fa2.FA2_ERR_WORKSPACE
+    assert "workspace" in fa2.strerror(fa2.FA2_ERR_WORKSPACE)
 
 
 def test_default_splits():
