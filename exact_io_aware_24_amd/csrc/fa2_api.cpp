@@ -43,14 +43,15 @@ int validate(const void *q, const void *k, const void *v, const void *o,
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || H_kv < 1 || H % H_kv != 0)
     return FA2_ERR_SHAPE;
   if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
-  const int64_t bh = static_cast<int64_t>(B) * H;
+  const int64_t bh = static_cast<int64_t>(B) * H;  // < 2^62: no overflow
   const int64_t q_head = static_cast<int64_t>(Nq) * d;
   const int64_t kv_head = static_cast<int64_t>(Nk) * d;
+  // bounded factors first, so that no product below can overflow int64
+  if (bh > INT32_MAX || q_head > max_per_head || kv_head > max_per_head)
+    return FA2_ERR_SHAPE;
   const int64_t blocks = bh * ((static_cast<int64_t>(Nq) + rows_per_block - 1) /
                                rows_per_block);
-  if (bh > INT32_MAX || q_head > max_per_head || kv_head > max_per_head ||
-      blocks > INT32_MAX || bh * q_head > FA2_MAX_ELEMS ||
-      bh * kv_head > FA2_MAX_ELEMS)
+  if (blocks > INT32_MAX || bh * q_head > FA2_MAX_ELEMS || bh * kv_head > FA2_MAX_ELEMS)
     return FA2_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA2_ERR_SCALE;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
@@ -310,7 +311,8 @@ FA2_EXPORT int fa2_quantize_fp8(const void *x, void *codes, int *exps, int B,
   if (d != 64 && d != 128) return FA2_ERR_HEADDIM;
   const int64_t bh = static_cast<int64_t>(B) * H;
   const int64_t nb = (static_cast<int64_t>(N) + block_rows - 1) / block_rows;
-  if (bh * nb > INT32_MAX || bh * N * d > FA2_MAX_ELEMS) return FA2_ERR_SHAPE;
+  if (bh > INT32_MAX || bh * nb > INT32_MAX || bh * N * d > FA2_MAX_ELEMS)
+    return FA2_ERR_SHAPE;
   if (misaligned(x) || misaligned(codes) || (reinterpret_cast<uintptr_t>(exps) & 3) ||
       (signs && (reinterpret_cast<uintptr_t>(signs) & 3)))
     return FA2_ERR_ALIGN;

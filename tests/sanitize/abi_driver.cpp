@@ -1,0 +1,174 @@
+// Host-only driver of the C-ABI validation layer (fa2_api.cpp), built with
+// AddressSanitizer and UndefinedBehaviorSanitizer.  The kernel launchers are
+// stubs that record the call: valid arguments must reach exactly one
+// launcher, invalid ones must be rejected with their code before any launch.
+// Exit status 0 when every check holds.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+
+#include "fa2.h"
+#include "fa2_internal.h"
+
+namespace {
+int g_launches = 0;
+hipError_t g_result = hipSuccess;
+alignas(256) float g_scratch[64];
+}  // namespace
+
+namespace fa2 {
+hipError_t launch_fwd_bf16(const FwdArgs &a, bool, hipStream_t) {
+  ++g_launches;
+  if (a.n_splits > 1 && (!a.o_part || !a.lse_part)) return hipErrorInvalidValue;
+  return g_result;
+}
+hipError_t launch_bwd_bf16(const BwdArgs &, bool, hipStream_t) { ++g_launches; return g_result; }
+hipError_t launch_fwd_fp32(const FwdArgs &, hipStream_t) { ++g_launches; return g_result; }
+hipError_t launch_quantize_fp8(const QuantArgs &, hipStream_t) { ++g_launches; return g_result; }
+hipError_t launch_fwd_fp8(const Fp8Args &, bool, hipStream_t) { ++g_launches; return g_result; }
+hipError_t fwd_scratch(float **ptr) { *ptr = g_scratch; return hipSuccess; }
+}  // namespace fa2
+
+static int g_fail = 0;
+#define EXPECT(expr, want)                                                    \
+  do {                                                                        \
+    const int before_ = g_launches;                                           \
+    const int got_ = (expr);                                                  \
+    const int launched_ = g_launches - before_;                               \
+    if (got_ != (want) || launched_ != ((want) == FA2_OK ? 1 : 0)) {          \
+      std::printf("FAIL line %d: %s -> %d (want %d), launches %d\n", __LINE__, \
+                  #expr, got_, (want), launched_);                            \
+      ++g_fail;                                                               \
+    }                                                                         \
+  } while (0)
+
+// fake, never dereferenced device addresses, 64 MiB apart
+static void *P(int i) { return reinterpret_cast<void *>(uintptr_t(0x10000000) + uintptr_t(i) * (64u << 20)); }
+static float *F(int i) { return static_cast<float *>(P(i)); }
+static void *off(void *p, int bytes) { return static_cast<char *>(p) + bytes; }
+
+int main() {
+  const float nan = std::numeric_limits<float>::quiet_NaN();
+  const float inf = std::numeric_limits<float>::infinity();
+  // forward entry points with the plain signature
+  typedef int (*fwd_fn)(const void *, const void *, const void *, void *, float *, int, int,
+                        int, int, float, int, void *);
+  fwd_fn fwds[2] = {fa2_fwd, reinterpret_cast<fwd_fn>(fa2_fwd_o32)};
+  for (fwd_fn f : fwds) {
+    EXPECT(f(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, nullptr), FA2_OK);
+    EXPECT(f(P(0), P(1), P(2), P(3), nullptr, 2, 3, 1000, 128, 0.1f, 1, nullptr), FA2_OK);
+    EXPECT(f(nullptr, P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, nullptr), FA2_ERR_NULL);
+    EXPECT(f(P(0), P(1), P(2), nullptr, F(4), 1, 2, 64, 64, 0.125f, 0, nullptr), FA2_ERR_NULL);
+    EXPECT(f(P(0), P(1), P(2), P(3), F(4), 0, 2, 64, 64, 0.125f, 0, nullptr), FA2_ERR_SHAPE);
+    EXPECT(f(P(0), P(1), P(2), P(3), F(4), 1, -2, 64, 64, 0.125f, 0, nullptr), FA2_ERR_SHAPE);
+    EXPECT(f(P(0), P(1), P(2), P(3), F(4), 1, 2, 1 << 30, 128, 0.125f, 0, nullptr), FA2_ERR_SHAPE);
+    EXPECT(f(P(0), P(1), P(2), P(3), F(4), 1 << 16, 1 << 16, 1, 64, 0.125f, 0, nullptr), FA2_ERR_SHAPE);
+    EXPECT(f(P(0), P(1), P(2), P(3), F(4), INT32_MAX, INT32_MAX, INT32_MAX, 128, 0.1f, 0, nullptr),
+           FA2_ERR_SHAPE);
+    EXPECT(f(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 96, 0.125f, 0, nullptr), FA2_ERR_HEADDIM);
+    EXPECT(f(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, nan, 0, nullptr), FA2_ERR_SCALE);
+    EXPECT(f(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, -inf, 0, nullptr), FA2_ERR_SCALE);
+    EXPECT(f(off(P(0), 8), P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.1f, 0, nullptr), FA2_ERR_ALIGN);
+    EXPECT(f(P(0), P(1), P(2), P(3), static_cast<float *>(off(F(4), 4)), 1, 2, 64, 64, 0.1f, 0,
+             nullptr), FA2_ERR_ALIGN);
+    EXPECT(f(P(0), P(1), P(2), P(0), F(4), 1, 2, 64, 64, 0.1f, 0, nullptr), FA2_ERR_ALIAS);
+    EXPECT(f(P(0), P(1), P(2), off(P(2), 4096), F(4), 1, 2, 64, 64, 0.1f, 0, nullptr), FA2_ERR_ALIAS);
+    EXPECT(f(P(0), P(1), P(2), P(3), static_cast<float *>(off(P(3), 16)), 1, 2, 64, 64, 0.1f, 0,
+           nullptr), FA2_ERR_ALIAS);
+  }
+  // fp32 entry point (element size 4)
+  EXPECT(fa2_fwd_fp32(F(0), F(1), F(2), F(3), F(4), 1, 1, 128, 64, 0.125f, 0, nullptr), FA2_OK);
+  EXPECT(fa2_fwd_fp32(F(0), F(1), F(2), static_cast<float *>(off(F(0), 16)), F(4), 1, 1, 128, 64,
+                      0.125f, 0, nullptr), FA2_ERR_ALIAS);
+  // grouped K/V heads
+  EXPECT(fa2_fwd_gqa(P(0), P(1), P(2), P(3), F(4), 2, 8, 2, 300, 128, 0.1f, 1, nullptr), FA2_OK);
+  EXPECT(fa2_fwd_gqa(P(0), P(1), P(2), P(3), F(4), 2, 8, 3, 300, 128, 0.1f, 1, nullptr), FA2_ERR_SHAPE);
+  EXPECT(fa2_fwd_gqa(P(0), P(1), P(2), P(3), F(4), 2, 8, 0, 300, 128, 0.1f, 1, nullptr), FA2_ERR_SHAPE);
+  // split key ranges, caller workspaces
+  EXPECT(fa2_fwd_splitkv(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1, 4, F(5),
+                         F(6), nullptr), FA2_OK);
+  EXPECT(fa2_fwd_splitkv(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1, 1, nullptr,
+                         nullptr, nullptr), FA2_OK);
+  EXPECT(fa2_fwd_splitkv(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1, 4, nullptr,
+                         F(6), nullptr), FA2_ERR_NULL);
+  EXPECT(fa2_fwd_splitkv(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1, 0, F(5),
+                         F(6), nullptr), FA2_ERR_SHAPE);
+  EXPECT(fa2_fwd_splitkv(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1,
+                         FA2_MAX_SPLITS + 1, F(5), F(6), nullptr), FA2_ERR_SHAPE);
+  EXPECT(fa2_fwd_splitkv(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1, 4, F(5),
+                         static_cast<float *>(off(F(5), 64)), nullptr), FA2_ERR_ALIAS);
+  EXPECT(fa2_fwd_splitkv_o32(F(0), F(1), F(2), F(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1, 4,
+                             F(5), static_cast<float *>(off(F(6), 4)), nullptr), FA2_ERR_ALIGN);
+  // the allocation-free variant: static workspace, size limit
+  EXPECT(fa2_fwd_splitkv_noalloc(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1, 4,
+                                 nullptr), FA2_OK);
+  EXPECT(fa2_fwd_splitkv_noalloc(P(0), P(1), P(2), P(3), F(4), 1, 1, 1, 1 << 16, 1 << 16, 128,
+                                 0.1f, 0, 2, nullptr), FA2_ERR_WORKSPACE);
+  EXPECT(fa2_fwd_splitkv_noalloc(P(0), P(1), P(2), nullptr, F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1,
+                                 4, nullptr), FA2_ERR_NULL);
+  EXPECT(fa2_fwd_splitkv_noalloc(P(0), P(1), P(2), P(3), F(4), INT32_MAX, INT32_MAX, 1, INT32_MAX,
+                                 INT32_MAX, 128, 0.1f, 1, 1024, nullptr), FA2_ERR_SHAPE);
+  EXPECT(fa2_bwd(P(0), P(1), P(2), P(3), P(4), F(5), F(6), P(7), P(8), P(9), INT32_MAX, INT32_MAX,
+                 INT32_MAX, 128, 0.1f, 1, nullptr), FA2_ERR_SHAPE);
+  // FP8 path
+  int *E0 = static_cast<int *>(P(5));
+  EXPECT(fa2_quantize_fp8(P(0), P(1), E0, 1, 2, 100, 128, 64, F(6), nullptr), FA2_OK);
+  EXPECT(fa2_quantize_fp8(P(0), P(1), E0, 1, 2, 100, 128, 32, F(6), nullptr), FA2_ERR_SHAPE);
+  EXPECT(fa2_quantize_fp8(P(0), P(1), E0, INT32_MAX, INT32_MAX, INT32_MAX, 128, 64, F(6), nullptr),
+         FA2_ERR_SHAPE);
+  EXPECT(fa2_quantize_fp8(P(0), off(P(0), 64), E0, 1, 2, 100, 128, 64, F(6), nullptr), FA2_ERR_ALIAS);
+  EXPECT(fa2_fwd_fp8(P(0), static_cast<int *>(P(1)), P(2), static_cast<int *>(P(3)), P(4),
+                     static_cast<int *>(P(5)), P(6), F(7), 1, 2, 100, 128, 0.1f, 1, 1, nullptr), FA2_OK);
+  EXPECT(fa2_fwd_fp8(P(0), nullptr, P(2), static_cast<int *>(P(3)), P(4),
+                     static_cast<int *>(P(5)), P(6), F(7), 1, 2, 100, 128, 0.1f, 1, 1, nullptr),
+         FA2_ERR_NULL);
+  EXPECT(fa2_fwd_fp8(P(0), static_cast<int *>(P(1)), P(2), static_cast<int *>(P(3)), P(4),
+                     static_cast<int *>(P(5)), P(1), F(7), 1, 2, 100, 128, 0.1f, 1, 1, nullptr),
+         FA2_ERR_ALIAS);
+  // backward
+  EXPECT(fa2_bwd(P(0), P(1), P(2), P(3), P(4), F(5), F(6), P(7), P(8), P(9), 1, 2, 200, 128, 0.1f,
+                 1, nullptr), FA2_OK);
+  EXPECT(fa2_bwd(P(0), P(1), P(2), P(3), P(4), nullptr, F(6), P(7), P(8), P(9), 1, 2, 200, 128,
+                 0.1f, 1, nullptr), FA2_ERR_NULL);
+  EXPECT(fa2_bwd(P(0), P(1), P(2), P(3), P(4), F(5), F(6), P(7), P(8), P(0), 1, 2, 200, 128, 0.1f,
+                 1, nullptr), FA2_ERR_ALIAS);
+  EXPECT(fa2_bwd(P(0), P(1), P(2), P(3), P(4), F(5), F(6), P(7), P(7), P(9), 1, 2, 200, 128, 0.1f,
+                 1, nullptr), FA2_ERR_ALIAS);
+  EXPECT(fa2_bwd_o32(P(0), P(1), P(2), P(3), P(4), F(5), F(6), F(7), F(8), F(9), 1, 2, 200, 64,
+                     0.1f, 0, nullptr), FA2_OK);
+  EXPECT(fa2_bwd_gqa(P(0), P(1), P(2), P(3), P(4), F(5), F(6), P(7), P(8), P(9), 2, 8, 2, 300, 128,
+                     0.1f, 1, 4, F(10), nullptr), FA2_OK);
+  EXPECT(fa2_bwd_gqa(P(0), P(1), P(2), P(3), P(4), F(5), F(6), P(7), P(8), P(9), 2, 8, 2, 300, 128,
+                     0.1f, 1, 5, F(10), nullptr), FA2_ERR_SHAPE);
+  EXPECT(fa2_bwd_gqa(P(0), P(1), P(2), P(3), P(4), F(5), F(6), P(7), P(8), P(9), 2, 8, 2, 300, 128,
+                     0.1f, 1, 4, nullptr, nullptr), FA2_ERR_NULL);
+  // a failing launch is reported as FA2_ERR_HIP
+  g_result = hipErrorLaunchFailure;
+  {
+    const int before = g_launches;
+    const int rc = fa2_fwd(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, nullptr);
+    if (rc != FA2_ERR_HIP || g_launches != before + 1) {
+      std::printf("FAIL: launch failure -> %d\n", rc);
+      ++g_fail;
+    }
+  }
+  g_result = hipSuccess;
+  // every code has its own message; unknown codes too
+  const int codes[] = {FA2_OK, FA2_ERR_NULL, FA2_ERR_SHAPE, FA2_ERR_HEADDIM, FA2_ERR_SCALE,
+                       FA2_ERR_ALIGN, FA2_ERR_ALIAS, FA2_ERR_HIP, FA2_ERR_WORKSPACE, 12345, -99};
+  for (int c : codes) {
+    const char *m = fa2_strerror(c);
+    if (!m || !std::strlen(m)) {
+      std::printf("FAIL: strerror(%d)\n", c);
+      ++g_fail;
+    }
+  }
+  if (fa2_version() != 7) {
+    std::printf("FAIL: version %d\n", fa2_version());
+    ++g_fail;
+  }
+  std::printf("%s: %d failures, %d launches\n", g_fail ? "FAILED" : "ok", g_fail, g_launches);
+  return g_fail ? 1 : 0;
+}
