@@ -125,15 +125,18 @@ def rocm_version() -> str:
 
 
 class ClockSampler:
-    """Engine (GFX) clock of the benchmarked GPU read through amdsmi while
-    the timed kernels run: the power limit lowers the clock under load, so
-    the achieved fraction of the 2.4 GHz peak mixes kernel efficiency with
-    the clock.  Every failure leaves the sampler disabled (``None`` in the
-    record); it never affects the timing itself."""
+    """Engine (GFX) clock of the benchmarked GPU, read through amdsmi's GPU
+    metrics (``current_gfxclks``: one value per XCD, averaged) while kernels
+    run: the power limit lowers the clock under load, so the achieved
+    fraction of the 2.4 GHz peak mixes kernel efficiency with the clock.
+    The firmware refreshes these metrics every few hundred milliseconds, so
+    a timed region shorter than that may only see values from before it;
+    the record says how many distinct readings it got.  Every failure
+    leaves the sampler disabled (``None`` in the record); it never affects
+    the timing itself."""
 
     def __init__(self, torch, dev):
         self.samples = []
-        self.source = None
         self._read = None
         try:
             import amdsmi
@@ -152,45 +155,42 @@ class ClockSampler:
             if handle is None:
                 return
 
-            def read_metrics():
+            def read():
                 m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
-                val = m.get("current_gfxclk", m.get("average_gfxclk_frequency"))
-                if isinstance(val, (list, tuple)):
-                    val = max(x for x in val if isinstance(x, (int, float)))
-                return float(val)
+                vals = [x for x in m.get("current_gfxclks", [])
+                        if isinstance(x, (int, float))]
+                if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+                    vals = [m["current_gfxclk"]]
+                return sum(vals) / len(vals) if vals else None
 
-            def read_clock():
-                return float(amdsmi.amdsmi_get_clock_info(
-                    handle, amdsmi.AmdSmiClkType.GFX)["clk"])
-
-            for fn, name in ((read_metrics, "amdsmi gpu metrics, current gfxclk"),
-                             (read_clock, "amdsmi clock info, GFX")):
-                try:
-                    v = fn()
-                    if 100.0 <= v <= 5000.0:
-                        self._read, self.source = fn, name
-                        break
-                except Exception:
-                    continue
+            read()
+            self._read = read
         except Exception:
             self._read = None
 
-    def poll_until(self, event, period_s=0.002):
-        """Sample until ``event`` has completed (the timed kernels drained)."""
+    def poll_until(self, event, period_s=0.005):
+        """Sample until ``event`` has completed (the kernels drained)."""
+        out = []
         while not event.query():
             if self._read is not None:
                 try:
-                    self.samples.append(self._read())
+                    v = self._read()
+                    if v is not None:
+                        out.append(float(v))
                 except Exception:
                     self._read = None
             time.sleep(period_s)
+        return out
 
-    def summary(self):
-        if not self.samples:
+    @staticmethod
+    def summary(samples):
+        if not samples:
             return None
-        s = sorted(self.samples)
-        return {"mean_mhz": round(sum(s) / len(s), 1), "min_mhz": s[0],
-                "max_mhz": s[-1], "samples": len(s), "source": self.source}
+        s = sorted(samples)
+        return {"mean_mhz": round(sum(s) / len(s), 1), "min_mhz": round(s[0], 1),
+                "max_mhz": round(s[-1], 1), "samples": len(s),
+                "distinct": len(set(s)),
+                "source": "amdsmi gpu metrics, current_gfxclks (mean over XCDs)"}
 
 
 def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
@@ -429,7 +429,7 @@ def main(argv=None):
     for _ in range(args.steps):
         step()
     end.record(stream)
-    clock.poll_until(end)
+    clock_timed = clock.poll_until(end)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
@@ -454,6 +454,19 @@ def main(argv=None):
                     "min_ms": round(per[0], 5),
                     "median_tflops": round(flops / (per[len(per) // 2] * 1e-3) / 1e12, 3),
                     "cold_mall_mib": args.cold_mall}
+
+    # the clock this kernel sustains: the same step for ~0.6 s after the
+    # timed region (not timed), sampled the same way
+    clock_load = []
+    if clock._read is not None:
+        n_load = max(1, int(math.ceil(0.6 / max(ms * 1e-3, 1e-6))))
+        n_load = min(n_load, 20000)
+        done = torch.cuda.Event()
+        for _ in range(n_load):
+            step()
+        done.record(stream)
+        clock_load = clock.poll_until(done)
+        torch.cuda.synchronize()
 
     default_entry = "fa2_fwd_splitkv" if decode else "fa2_" + args.which
     same_shape = not args.seq_len and not args.splits and not args.gsplits and \
@@ -493,7 +506,8 @@ def main(argv=None):
         "compulsory_hbm_bytes": comp,
         "kernel_source_sha256": kernel_source_hash("fp8" if fp8 else args.which),
         "gpu": torch.cuda.get_device_name(dev),
-        "gfx_clock_during_timed_steps": clock.summary(),
+        "gfx_clock_during_timed_steps": clock.summary(clock_timed),
+        "gfx_clock_sustained_after_timing": clock.summary(clock_load[len(clock_load) // 2:]),
         "rocm": rocm_version(),
         "torch": torch.__version__,
         "seed": wl.DEFAULT_SEED,

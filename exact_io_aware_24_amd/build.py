@@ -24,6 +24,11 @@ ARCH = "gfx950"
 
 SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_fp32.hip", "fa2_bwd_bf16.hip",
            "fa2_fp8.hip"]
+# Per-source flags.  The bf16 forward is scheduled with LLVM's
+# "max-memory-clause" machine-scheduler strategy: same instructions and
+# registers (no spills), 0.5-1.5 % faster on every forward workload than the
+# default strategy in same-process A/B timing.
+SOURCE_FLAGS = {"fa2_fwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 
 def hipcc() -> str:
@@ -51,7 +56,7 @@ def build(verbose: bool = False, out: str = LIB_PATH, extra=()) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-            cmd = [cc] + compile_flags(extra) + lang + [
+            cmd = [cc] + compile_flags(list(SOURCE_FLAGS.get(src, [])) + list(extra)) + lang + [
                 "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
