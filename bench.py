@@ -295,6 +295,9 @@ def main(argv=None):
                     help="also time single calls (median, min)")
     ap.add_argument("--cold-mall", type=int, default=0, metavar="MIB",
                     help="with --per-call: write this many MiB between calls")
+    ap.add_argument("--clock-window", type=float, default=2.5, metavar="S",
+                    help="seconds of untimed load after the timed steps during which "
+                         "the engine clock is sampled (0: none)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter "
                          "calibration runs)")
@@ -455,18 +458,21 @@ def main(argv=None):
                     "median_tflops": round(flops / (per[len(per) // 2] * 1e-3) / 1e12, 3),
                     "cold_mall_mib": args.cold_mall}
 
-    # the clock this kernel sustains: the same step for ~0.6 s after the
-    # timed region (not timed), sampled the same way
+    # the clock this kernel sustains: the same step for --clock-window seconds
+    # after the timed region (not timed), sampled the same way; the firmware
+    # refreshes the reading about once a second, so only the samples of the
+    # last 60 % of the window are kept
     clock_load = []
-    if clock._read is not None:
-        n_load = max(1, int(math.ceil(0.6 / max(ms * 1e-3, 1e-6))))
-        n_load = min(n_load, 20000)
+    if clock._read is not None and args.clock_window > 0:
+        n_load = max(1, int(math.ceil(args.clock_window / max(ms * 1e-3, 1e-6))))
+        n_load = min(n_load, 100000)
         done = torch.cuda.Event()
         for _ in range(n_load):
             step()
         done.record(stream)
         clock_load = clock.poll_until(done)
         torch.cuda.synchronize()
+        clock_load = clock_load[int(0.4 * len(clock_load)):]
 
     default_entry = "fa2_fwd_splitkv" if decode else "fa2_" + args.which
     same_shape = not args.seq_len and not args.splits and not args.gsplits and \
@@ -507,7 +513,7 @@ def main(argv=None):
         "kernel_source_sha256": kernel_source_hash("fp8" if fp8 else args.which),
         "gpu": torch.cuda.get_device_name(dev),
         "gfx_clock_during_timed_steps": clock.summary(clock_timed),
-        "gfx_clock_sustained_after_timing": clock.summary(clock_load[len(clock_load) // 2:]),
+        "gfx_clock_sustained_after_timing": clock.summary(clock_load),
         "rocm": rocm_version(),
         "torch": torch.__version__,
         "seed": wl.DEFAULT_SEED,
