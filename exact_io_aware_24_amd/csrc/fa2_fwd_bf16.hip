@@ -36,7 +36,8 @@
 // the stated tolerance on sharp softmaxes (the x20 outlier rows).  The lse
 // keeps the fp32 sum of the unrounded values.
 //
-// gfx950 mapping (this library's design, not the pages'):
+// gfx950 mapping (this library's design, not the pages'), fwd_bf16_kernel
+// (d = 128; d = 64 runs fwd_small_kernel, further down):
 //  * 256 threads = 4 wave64s; wave w owns query rows [32w, 32w+32) of the
 //    block, so the softmax statistics of a row never leave its wave (the
 //    wiki article's improvement 3: no shared-memory exchange between warps
@@ -406,8 +407,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int xcd = static_cast<int>(blockIdx.x & 7);
   const int ilo = static_cast<int>(static_cast<int64_t>(xcd) * p.total / 8);
   const int ilen = static_cast<int>(static_cast<int64_t>(xcd + 1) * p.total / 8) - ilo;
-  // (d = 64 never walks: the item loop's extra live registers would spill)
-  constexpr bool kCanPersist = D == 128;
+  constexpr bool kCanPersist = D == 128;  // (d = 64 runs fwd_small_kernel)
   auto item_at = [&](int r) -> int {
     if (!kCanPersist || !p.persist) return r == 0 ? xcd_remap(blockIdx.x, p.total) : -1;
     const int local = r * per + ((r & 1) ? per - 1 - xj : xj);
@@ -644,6 +644,321 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   }
 }
 
+// ---- d = 64: four waves per SIMD ---------------------------------------------------
+//
+// At d = 64 a score costs half the matrix work of d = 128 for the same
+// softmax work, so the kernel is bound by its VALU issue: what pays is more
+// waves to issue from and less VALU work per score.  fwd_small_kernel keeps
+// the work items, the per-wave ownership of 32 query rows, the operand
+// layouts and the normaliser of fwd_bf16_kernel, with
+//  * 64-key tiles double-buffered in LDS (2 x 16 KB) and no score of the next
+//    tile in flight: 120-128 VGPRs, four waves per SIMD;
+//  * the checked softmax: a tile's exponentials are taken against the
+//    current reference first, and only if some lane's sum of them exceeds
+//    2^16 (or is not finite: the first tile, whose reference is still -inf)
+//    does the wave find the tile's row maxima, raise the reference to them,
+//    rescale l, the rounded sum and O~, and take the exponentials again.
+//    Every P~ that reaches the sums is then <= 2^16; the row maximum (16
+//    max3 per lane and tile, a cross-lane step, a ballot) leaves the common
+//    path.  With O~ divided by the sum of the rounded P~, how far the
+//    largest P~ sits from 1 no longer affects the error.
+constexpr int kSmallTile = 64;
+constexpr float kCheckedSumLimit = 65536.0f;  // 2^16
+
+template <int D, int BC_>
+struct Cfg3 {
+  static constexpr int BC = BC_;                      // keys per tile
+  static constexpr int NKT = BC / 32;                 // 32-key sub-tiles
+  static constexpr int KCH = D / 8;                   // 16-byte granules per K row
+  static constexpr int NDT = D / 16;                  // 16-dim MFMA k-steps (S)
+  static constexpr int NCT = D / 32;                  // 32-wide O^T row tiles
+  static constexpr int TILE_BYTES = BC * D * 2;       // K or V tile
+  static constexpr int NLOAD = TILE_BYTES / 1024 / 4; // 1 KB loads per wave per operand
+  static constexpr int K_ROWS_PER_LOAD = 64 / KCH;    // K rows per 1 KB load
+  static constexpr int VGROUPS = BC / 16;             // 16-key groups per V column block
+  static constexpr int NSTAGE = 2;                   // double-buffered
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V
+  static_assert(NLOAD >= 1 && NLOAD * 4 * 1024 == TILE_BYTES, "tile loads");
+};
+
+template <int D, int BC>
+struct Offsets3 {
+  using C = Cfg3<D, BC>;
+  int k_rd[C::NDT];
+  int v_rd;
+  int k_ld[C::NLOAD], v_ld[C::NLOAD];
+  int k_dst[C::NLOAD], v_dst[C::NLOAD];
+};
+
+template <int D, int BC>
+__device__ __forceinline__ void issue_tile3(const uint16_t *kh, const uint16_t *vh,
+                                            int head_bytes, const Offsets3<D, BC> &off,
+                                            char *stage, int tile_byte) {
+  using C = Cfg3<D, BC>;
+  const u32x4 rk = tile_desc(kh, head_bytes, tile_byte);
+  const u32x4 rv = tile_desc(vh, head_bytes, tile_byte);
+#pragma unroll
+  for (int it = 0; it < C::NLOAD; ++it)
+    dma16(rk, off.k_ld[it], 0, lds_addr(stage + off.k_dst[it]));
+#pragma unroll
+  for (int it = 0; it < C::NLOAD; ++it)
+    dma16(rv, off.v_ld[it], 0, lds_addr(stage + C::TILE_BYTES + off.v_dst[it]));
+}
+
+template <int D, int BC>
+struct WaveState3 {
+  using C = Cfg3<D, BC>;
+  bf16x8 qreg[C::NDT];
+  f32x16 oacc[C::NCT];
+  float m_run, l_run, lr_run;
+};
+
+// S^T of one tile (MFMA), mask, checked softmax, sums, P~.V (MFMA).
+template <int D, int BC, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void tile3(const char *sb, const Offsets3<D, BC> &off,
+                                      WaveState3<D, BC> &st, float c, int j0, int N, int qi,
+                                      int hh) {
+  using C = Cfg3<D, BC>;
+  f32x16 s[C::NKT];
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt) {
+      const bf16x8 a = lds_load<bf16x8>(sb, off.k_rd[dt] + kt * 32 * D * 2);
+      s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qreg[dt], s[kt], 0, 0, 0);
+    }
+  if (MASKED) {
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= N || (CAUSAL && key > qi)) s[kt][r] = -INFINITY;
+      }
+  }
+  auto raise = [&]() {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    float mlo, mhi;
+    halves(mx, mlo, mhi);
+    mx = fmaxf(mlo, mhi);
+    const float m_tile = (MASKED && mx == -INFINITY) ? -INFINITY : mx * c;
+    return m_tile;
+  };
+  auto rescale = [&](float m_tile) {
+    const float m_new = fmaxf(st.m_run, m_tile);
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= alpha;
+    st.lr_run *= alpha;
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.oacc[ct][r] *= alpha;
+  };
+  bf16x8 pb[C::NKT][2];
+  auto exps = [&](float mu) -> float {
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sv = s[kt][8 * u + e];
+          float x = fast_exp2(__builtin_fmaf(sv, c, -mu));
+          if (MASKED) x = (sv == -INFINITY) ? 0.f : x;
+          rs += x;
+          pb[kt][u][e] = static_cast<__bf16>(x);
+        }
+    return rs;
+  };
+  float rs = exps(st.m_run);
+  if (__builtin_amdgcn_ballot_w64(!(rs <= kCheckedSumLimit))) {
+    rescale(raise());
+    rs = exps(st.m_run == -INFINITY ? 0.f : st.m_run);
+  }
+  st.l_run += rs;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  float rr = st.lr_run;
+#pragma unroll
+  for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pb[kt][u][e], pb[kt][u][e + 1]};
+        rr = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rr, false);
+      }
+  st.lr_run = rr;
+  const char *vb = sb + C::TILE_BYTES;
+#pragma unroll
+  for (int ks = 0; ks < 2 * C::NKT; ++ks) {
+    bf16x8 a[C::NCT];
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct) {
+      const int imm = ct * C::BC * 64 + 16 * ks * 64;
+      const s16x4 lo = lds_read_tr(vb, off.v_rd + imm);
+      const s16x4 hi = lds_read_tr(vb, off.v_rd + imm + 8 * 64);
+      a[ct] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+      st.oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ct], pb[ks >> 1][ks & 1],
+                                                            st.oacc[ct], 0, 0, 0);
+  }
+}
+
+template <int D, int BC, bool CAUSAL, bool O32>
+__global__ __launch_bounds__(kThreads, 4) void fwd_small_kernel(Params p) {
+  using C = Cfg3<D, BC>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE_BYTES];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31;
+  const int hh = lane >> 5;
+  const int Nq = p.nq, Nk = p.nk;
+  const int qoff = Nk - Nq;
+  const int head_bytes = Nk * D * 2;
+
+  Offsets3<D, BC> off;
+#pragma unroll
+  for (int dt = 0; dt < C::NDT; ++dt)
+    off.k_rd[dt] = (lr * D + (((2 * dt + hh) ^ kswz<D>(lr)) * 8)) * 2;
+  {
+    const int g = lane >> 4, sl = lane & 15;
+    off.v_rd = (4 * hh + (sl >> 2)) * 64 + (g & 1) * 32 + (sl & 3) * 8;
+  }
+#pragma unroll
+  for (int it = 0; it < C::NLOAD; ++it) {
+    const int inst = wv * C::NLOAD + it;
+    const int row = inst * C::K_ROWS_PER_LOAD + lane / C::KCH;
+    const int pos = lane % C::KCH;
+    off.k_ld[it] = row * D * 2 + ((pos ^ kswz<D>(row)) * 16);
+    off.k_dst[it] = inst * 1024;
+    const int cg = inst / C::VGROUPS, kb = inst % C::VGROUPS;
+    off.v_ld[it] = (16 * kb + lane / 4) * D * 2 + (4 * cg + (lane & 3)) * 16;
+    off.v_dst[it] = cg * C::BC * 64 + kb * 1024;
+  }
+  float c = p.c;
+  uint32_t qflip = 0;
+  if (c < 0.f) {
+    c = -c;
+    qflip = 0x80008000u;
+  }
+  auto stage = [&](int t) { return smem + (t % C::NSTAGE) * C::STAGE_BYTES; };
+  int split, bh, q0;
+  {
+    int logical = xcd_remap(blockIdx.x, p.total);
+    split = 0;
+    if (p.n_splits > 1) {
+      split = logical % p.n_splits;
+      logical /= p.n_splits;
+    }
+    bh = logical / p.n_qblocks;
+    const int qbl = logical - bh * p.n_qblocks;
+    q0 = (CAUSAL ? (p.n_qblocks - 1 - qbl) : qbl) * kRows;
+  }
+  const int kvbh = p.group == 1 ? bh : (bh / p.h) * (p.h / p.group) + (bh % p.h) / p.group;
+  const size_t kvhead = static_cast<size_t>(kvbh) * Nk * D;
+  const uint16_t *kh = p.k + kvhead;
+  const uint16_t *vh = p.v + kvhead;
+  const int qw = q0 + wv * 32;
+  const int qi = qw + lr;
+  const int qpos = qi + qoff;
+  WaveState3<D, BC> st;
+  {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.q + static_cast<size_t>(bh) * Nq * D), 0, Nq * D * 2,
+        kBufWord3);
+    const int q_ld = ((qw + lr) * D + 8 * hh) * 2;
+#pragma unroll
+    for (int t = 0; t < C::NDT; ++t)
+      st.qreg[t] = __builtin_bit_cast(
+          bf16x8, __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rq, q_ld + 32 * t, 0, 0)) ^ qflip);
+  }
+#pragma unroll
+  for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.oacc[ct][r] = 0.f;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+  st.lr_run = 0.f;
+  const int kend = CAUSAL ? max(0, min(Nk, q0 + kRows + qoff)) : Nk;
+  const int tb = split * p.tiles_per_split;
+  const int ntiles = min((kend + C::BC - 1) / C::BC, tb + p.tiles_per_split);
+  const int n_full = CAUSAL ? max(0, (q0 + qoff + 1) / C::BC) : Nk / C::BC;
+  const bool live = qw < Nq;
+  const int w_tiles = !live ? tb
+                      : CAUSAL ? min(ntiles, (qw + 31 + qoff) / C::BC + 1) : ntiles;
+  const int n_main = live ? min(n_full, ntiles) : tb;
+  if (tb < ntiles) {
+    if (Nk % C::BC != 0) {
+      for (int i = tid; i < C::NSTAGE * C::STAGE_BYTES / 16; i += kThreads)
+        reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
+    issue_tile3<D, BC>(kh, vh, head_bytes, off, stage(tb), tb * C::BC * D * 2);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto step = [&](auto masked_tag, int t) {
+      constexpr bool M = decltype(masked_tag)::value;
+      const int j0 = t * C::BC;
+      if (t + 1 < ntiles)
+        issue_tile3<D, BC>(kh, vh, head_bytes, off, stage(t + 1), (j0 + C::BC) * D * 2);
+      if (t < w_tiles) tile3<D, BC, CAUSAL, M>(stage(t), off, st, c, j0, Nk, qpos, hh);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    using F = std::integral_constant<bool, false>;
+    using T = std::integral_constant<bool, true>;
+    int t = tb;
+    for (; t < n_main; ++t) step(F{}, t);
+    for (; t < ntiles; ++t) step(T{}, t);
+  }
+  float llo, lhi, rlo, rhi;
+  halves(st.l_run, llo, lhi);
+  halves(st.lr_run, rlo, rhi);
+  const float l_tot = llo + lhi;
+  const float lr_tot = rlo + rhi;
+  const float inv = lr_tot > 0.f ? 1.0f / lr_tot : 0.f;
+  if (qi < Nq) {
+    const size_t head = static_cast<size_t>(bh) * Nq * D + split * p.o_split_stride;
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int col = 32 * ct + 8 * a + 4 * hh;
+        const size_t o_off = head + static_cast<size_t>(qi) * D + col;
+        if (O32) {
+          f32x4 ov;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) ov[b] = st.oacc[ct][4 * a + b] * inv;
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + o_off) = ov;
+        } else {
+          __bf16 ob[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) ob[b] = static_cast<__bf16>(st.oacc[ct][4 * a + b] * inv);
+          *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p.o) + o_off) =
+              __builtin_bit_cast(u32x2, ob);
+        }
+      }
+    if (p.lse && hh == 0)
+      p.lse[split * p.lse_split_stride + static_cast<size_t>(bh) * Nq + qi] =
+          l_tot > 0.f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
 // ---- merge of key ranges -----------------------------------------------------
 //
 // Key range s of a query row left O_s = O~_s / l_s (fp32) and lse_s = m_s +
@@ -691,10 +1006,16 @@ __global__ __launch_bounds__(kThreads) void merge_splits_kernel(
   if (lse && col == 0) lse[row] = l > 0.f ? m + __logf(l) : -INFINITY;
 }
 
+// d = 128: fwd_bf16_kernel (two waves per SIMD, 64-key tiles, S(t+1) in
+// flight); d = 64: fwd_small_kernel (four waves per SIMD, 64-key tiles).
 template <int D, bool CAUSAL, bool O32>
 hipError_t launch(const Params &prm, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, O32>), dim3(grid),
-                     dim3(kThreads), 0, s, prm);
+  if constexpr (D == 64)
+    hipLaunchKernelGGL((fwd_small_kernel<D, kSmallTile, CAUSAL, O32>), dim3(grid),
+                       dim3(kThreads), 0, s, prm);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, O32>), dim3(grid),
+                       dim3(kThreads), 0, s, prm);
   return hipGetLastError();
 }
 
@@ -776,7 +1097,7 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s) {
   prm.group = a.group;
   prm.n_qblocks = (a.nq + kRows - 1) / kRows;
   prm.n_splits = a.n_splits;
-  const int bc = a.d == 128 ? Cfg<128>::BC : Cfg<64>::BC;
+  const int bc = a.d == 128 ? Cfg<128>::BC : kSmallTile;
   const int key_tiles = (a.nk + bc - 1) / bc;
   prm.tiles_per_split = (key_tiles + a.n_splits - 1) / a.n_splits;
   prm.total = a.bh * prm.n_qblocks * a.n_splits;
