@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t *o,
 // The lse and D values of a tile are staged in LDS next to it (rows past
 // the sequence end read as 0, which gives them zero weight because their
 // Q and dO rows are zero too).
-template <int D, bool CAUSAL, bool O32>
+template <int D, bool CAUSAL, bool O32, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
   using C = BCfg<D>;
   // [Q 0][Q 1][dO 0][dO 1][lse 0][lse 1][D 0][D 1] (statistics: 1 KB each,
@@ -355,21 +355,38 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
       *l = *l * kLog2e;
     }
   };
-  if (t0 < nt) issue(0, t0, 0);
+  // Order of the (head, query tile) steps.  One query head: tiles upward
+  // from the block's first.  Several (GROUPED): tiles from the last one down
+  // to the block's first, the range's heads interleaved at each tile, so
+  // that every workgroup of a (K/V head, head range) starts at the same tile
+  // and they move down together: a tile's Q and dO are fetched once for all
+  // of them and stay in L2 while they are read (walking up head by head,
+  // each workgroup starts at its own diagonal tile, and the range's Q/dO,
+  // twice an XCD's L2, is streamed again for every workgroup).
+  if (t0 < nt) issue(0, GROUPED ? nt - 1 : t0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   lse_to_base2(0);
   __syncthreads();
 
   const float c = p.c;
-  // One (head, tile) step, the next pair's tile prefetched (head-major
-  // order).  MASKED: the tile holds a query before one of the block's keys
-  // (causal, t < t_full) -- a compile-time switch, so that the other tiles
-  // carry no mask instructions.
+  // One (head, tile) step, the next pair's tile prefetched (tiles
+  // descending, heads ascending within a tile).  MASKED: the tile holds a
+  // query before one of the block's keys (causal, t < t_full) -- a
+  // compile-time switch, so that the other tiles carry no mask
+  // instructions.
   int b = 0;
   auto step = [&](auto masked_tag, int g, int t) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    if (t + 1 < nt) issue(g, t + 1, b ^ 1);
-    else if (g + 1 < ng) issue(g + 1, t0, b ^ 1);
+    bool next;
+    if (GROUPED) {
+      next = g + 1 < ng || t > t0;
+      if (g + 1 < ng) issue(g + 1, t, b ^ 1);
+      else if (t > t0) issue(0, t - 1, b ^ 1);
+    } else {
+      next = t + 1 < nt || g + 1 < ng;
+      if (t + 1 < nt) issue(g, t + 1, b ^ 1);
+      else if (g + 1 < ng) issue(g + 1, t0, b ^ 1);
+    }
     // this wave's keys all come after every query of the tile: nothing to do
     const bool skip = CAUSAL && (t * kTileRows + kTileRows - 1 < kw);
     if (!skip) {
@@ -411,15 +428,22 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    if (t + 1 < nt || g + 1 < ng) lse_to_base2(b ^ 1);
+    if (next) lse_to_base2(b ^ 1);
     __syncthreads();
     b ^= 1;
   };
   const int t_mask_end = CAUSAL ? min(t_full, nt) : t0;
-  for (int g = 0; g < ng; ++g) {
-    int t = t0;
-    for (; t < t_mask_end; ++t) step(std::true_type{}, g, t);
-    for (; t < nt; ++t) step(std::false_type{}, g, t);
+  if constexpr (GROUPED) {
+    for (int t = nt - 1; t >= t_mask_end; --t)
+      for (int g = 0; g < ng; ++g) step(std::false_type{}, g, t);
+    for (int t = t_mask_end - 1; t >= t0; --t)
+      for (int g = 0; g < ng; ++g) step(std::true_type{}, g, t);
+  } else {
+    for (int g = 0; g < ng; ++g) {
+      int t = t0;
+      for (; t < t_mask_end; ++t) step(std::true_type{}, g, t);
+      for (; t < nt; ++t) step(std::false_type{}, g, t);
+    }
   }
 
   if (kj < N) {
@@ -588,8 +612,12 @@ hipError_t launch(const BwdParams &prm, int64_t rows, hipStream_t s) {
                      0, s, prm.o, prm.dout, prm.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, O32>), dim3(prm.total_kv), dim3(kThreads),
-                     0, s, prm);
+  if (prm.group > prm.n_gsplits)  // some range holds several query heads
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, O32, true>), dim3(prm.total_kv),
+                       dim3(kThreads), 0, s, prm);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, O32, false>), dim3(prm.total_kv),
+                       dim3(kThreads), 0, s, prm);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (prm.n_gsplits > 1) {
