@@ -666,7 +666,7 @@ constexpr int kSmallTile = 64;
 constexpr float kCheckedSumLimit = 65536.0f;  // 2^16
 
 template <int D, int BC_>
-struct Cfg3 {
+struct SmallCfg {
   static constexpr int BC = BC_;                      // keys per tile
   static constexpr int NKT = BC / 32;                 // 32-key sub-tiles
   static constexpr int KCH = D / 8;                   // 16-byte granules per K row
@@ -682,8 +682,8 @@ struct Cfg3 {
 };
 
 template <int D, int BC>
-struct Offsets3 {
-  using C = Cfg3<D, BC>;
+struct SmallOffsets {
+  using C = SmallCfg<D, BC>;
   int k_rd[C::NDT];
   int v_rd;
   int k_ld[C::NLOAD], v_ld[C::NLOAD];
@@ -691,10 +691,10 @@ struct Offsets3 {
 };
 
 template <int D, int BC>
-__device__ __forceinline__ void issue_tile3(const uint16_t *kh, const uint16_t *vh,
-                                            int head_bytes, const Offsets3<D, BC> &off,
+__device__ __forceinline__ void issue_small_tile(const uint16_t *kh, const uint16_t *vh,
+                                            int head_bytes, const SmallOffsets<D, BC> &off,
                                             char *stage, int tile_byte) {
-  using C = Cfg3<D, BC>;
+  using C = SmallCfg<D, BC>;
   const u32x4 rk = tile_desc(kh, head_bytes, tile_byte);
   const u32x4 rv = tile_desc(vh, head_bytes, tile_byte);
 #pragma unroll
@@ -706,8 +706,8 @@ __device__ __forceinline__ void issue_tile3(const uint16_t *kh, const uint16_t *
 }
 
 template <int D, int BC>
-struct WaveState3 {
-  using C = Cfg3<D, BC>;
+struct SmallState {
+  using C = SmallCfg<D, BC>;
   bf16x8 qreg[C::NDT];
   f32x16 oacc[C::NCT];
   float m_run, l_run, lr_run;
@@ -715,10 +715,10 @@ struct WaveState3 {
 
 // S^T of one tile (MFMA), mask, checked softmax, sums, P~.V (MFMA).
 template <int D, int BC, bool CAUSAL, bool MASKED>
-__device__ __forceinline__ void tile3(const char *sb, const Offsets3<D, BC> &off,
-                                      WaveState3<D, BC> &st, float c, int j0, int N, int qi,
+__device__ __forceinline__ void small_tile(const char *sb, const SmallOffsets<D, BC> &off,
+                                      SmallState<D, BC> &st, float c, int j0, int N, int qi,
                                       int hh) {
-  using C = Cfg3<D, BC>;
+  using C = SmallCfg<D, BC>;
   f32x16 s[C::NKT];
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt)
@@ -819,7 +819,7 @@ __device__ __forceinline__ void tile3(const char *sb, const Offsets3<D, BC> &off
 
 template <int D, int BC, bool CAUSAL, bool O32>
 __global__ __launch_bounds__(kThreads, 4) void fwd_small_kernel(Params p) {
-  using C = Cfg3<D, BC>;
+  using C = SmallCfg<D, BC>;
   __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE_BYTES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -830,7 +830,7 @@ __global__ __launch_bounds__(kThreads, 4) void fwd_small_kernel(Params p) {
   const int qoff = Nk - Nq;
   const int head_bytes = Nk * D * 2;
 
-  Offsets3<D, BC> off;
+  SmallOffsets<D, BC> off;
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt)
     off.k_rd[dt] = (lr * D + (((2 * dt + hh) ^ kswz<D>(lr)) * 8)) * 2;
@@ -875,7 +875,7 @@ __global__ __launch_bounds__(kThreads, 4) void fwd_small_kernel(Params p) {
   const int qw = q0 + wv * 32;
   const int qi = qw + lr;
   const int qpos = qi + qoff;
-  WaveState3<D, BC> st;
+  SmallState<D, BC> st;
   {
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(p.q + static_cast<size_t>(bh) * Nq * D), 0, Nq * D * 2,
@@ -908,15 +908,15 @@ __global__ __launch_bounds__(kThreads, 4) void fwd_small_kernel(Params p) {
         reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
       __syncthreads();
     }
-    issue_tile3<D, BC>(kh, vh, head_bytes, off, stage(tb), tb * C::BC * D * 2);
+    issue_small_tile<D, BC>(kh, vh, head_bytes, off, stage(tb), tb * C::BC * D * 2);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     auto step = [&](auto masked_tag, int t) {
       constexpr bool M = decltype(masked_tag)::value;
       const int j0 = t * C::BC;
       if (t + 1 < ntiles)
-        issue_tile3<D, BC>(kh, vh, head_bytes, off, stage(t + 1), (j0 + C::BC) * D * 2);
-      if (t < w_tiles) tile3<D, BC, CAUSAL, M>(stage(t), off, st, c, j0, Nk, qpos, hh);
+        issue_small_tile<D, BC>(kh, vh, head_bytes, off, stage(t + 1), (j0 + C::BC) * D * 2);
+      if (t < w_tiles) small_tile<D, BC, CAUSAL, M>(stage(t), off, st, c, j0, Nk, qpos, hh);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
