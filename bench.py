@@ -514,6 +514,10 @@ def main(argv=None):
         "gpu": torch.cuda.get_device_name(dev),
         "gfx_clock_during_timed_steps": clock.summary(clock_timed),
         "gfx_clock_sustained_after_timing": clock.summary(clock_load),
+        "gfx_clock_note": ("amdsmi refreshes the engine clock reading about once a "
+                           "second: readings during a shorter timed region may "
+                           "predate it; the sustained figure is taken over the last "
+                           "60 % of --clock-window seconds of the same step, untimed"),
         "rocm": rocm_version(),
         "torch": torch.__version__,
         "seed": wl.DEFAULT_SEED,
