@@ -81,6 +81,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cstdlib>
 #include <mutex>
 #include <type_traits>
 
@@ -109,6 +110,8 @@ struct Params {
   int tiles_per_split;   // key tiles per range
   int total;             // bh * n_qblocks * n_splits (work items)
   int persist;           // 1: the grid walks the items (see the kernel)
+  int no_skip;           // 1: causal blocks also run the key tiles past
+                         // their diagonal, every score masked (test switch)
   size_t o_split_stride;    // elements between the partial outputs of splits
   size_t lse_split_stride;  // same for lse
   float c;               // scale * log2(e)
@@ -432,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   };
   // key tiles the query block starting at q0 needs (causal: up to its last query)
   auto block_tiles = [&](int q0) -> int {
-    const int kend = CAUSAL ? max(0, min(Nk, q0 + kRows + qoff)) : Nk;
+    const int kend = CAUSAL && !p.no_skip ? max(0, min(Nk, q0 + kRows + qoff)) : Nk;
     return (kend + C::BC - 1) / C::BC;
   };
 
@@ -492,7 +495,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     const bool live = qw < Nq;
     // tiles this wave needs (causal: keys up to its last query)
     const int w_tiles = !live ? tb
-                        : CAUSAL ? min(ntiles, (qw + 31 + qoff) / C::BC + 1) : ntiles;
+                        : CAUSAL && !p.no_skip ? min(ntiles, (qw + 31 + qoff) / C::BC + 1)
+                                               : ntiles;
     // branch-free main loop: tiles t and t+1 unmasked
     const int n_main = live ? min(n_full, ntiles) - 1 : tb;
     f32x16 sa[C::NKT], sb[C::NKT];
@@ -894,13 +898,14 @@ __global__ __launch_bounds__(kThreads, 4) void fwd_small_kernel(Params p) {
   st.m_run = -INFINITY;
   st.l_run = 0.f;
   st.lr_run = 0.f;
-  const int kend = CAUSAL ? max(0, min(Nk, q0 + kRows + qoff)) : Nk;
+  const int kend = CAUSAL && !p.no_skip ? max(0, min(Nk, q0 + kRows + qoff)) : Nk;
   const int tb = split * p.tiles_per_split;
   const int ntiles = min((kend + C::BC - 1) / C::BC, tb + p.tiles_per_split);
   const int n_full = CAUSAL ? max(0, (q0 + qoff + 1) / C::BC) : Nk / C::BC;
   const bool live = qw < Nq;
   const int w_tiles = !live ? tb
-                      : CAUSAL ? min(ntiles, (qw + 31 + qoff) / C::BC + 1) : ntiles;
+                      : CAUSAL && !p.no_skip ? min(ntiles, (qw + 31 + qoff) / C::BC + 1)
+                                             : ntiles;
   const int n_main = live ? min(n_full, ntiles) : tb;
   if (tb < ntiles) {
     if (Nk % C::BC != 0) {
@@ -1086,6 +1091,15 @@ hipError_t fwd_scratch(float **ptr) {
   return hipSuccess;
 }
 
+// FA2_DEBUG_NO_SKIP=1 in the environment (read at every call) makes causal
+// query blocks run the key tiles past their diagonal too, through the masked
+// path, where every score is hidden and adds exactly zero: a test of the
+// tile skipping, which must not change any output.
+static int debug_no_skip() {
+  const char *e = std::getenv("FA2_DEBUG_NO_SKIP");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s) {
   Params prm;
   prm.q = static_cast<const uint16_t *>(a.q);
@@ -1102,6 +1116,7 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s) {
   prm.tiles_per_split = (key_tiles + a.n_splits - 1) / a.n_splits;
   prm.total = a.bh * prm.n_qblocks * a.n_splits;
   prm.c = a.scale * kLog2e;
+  prm.no_skip = debug_no_skip();
   // A grid of two workgroups per compute unit walks the items when there
   // are more items than that and every item starts at key tile 0 with whole
   // tiles (d = 128, one key range, equal query and key lengths, no ragged

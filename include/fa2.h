@@ -97,6 +97,12 @@ extern "C" {
  * Products of bf16 values are exact in fp32; S and the running statistics
  * are fp32, probabilities are rounded to bf16 for the P.V product, whose
  * accumulation is fp32.
+ * Causal key tiles that lie entirely past a query block's last query are
+ * skipped: the mask hides every score in them, so they contribute exactly
+ * zero to l and to O.  With FA2_DEBUG_NO_SKIP=1 in the environment at the
+ * time of a call, the bf16 forward entry points (fa2_fwd, _o32, _gqa,
+ * _splitkv and its variants) compute those tiles too, every score masked;
+ * the outputs must not change.  It is a test switch and costs time.
  */
 int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
             int B, int H, int N, int d, float scale, int causal, void *stream);
