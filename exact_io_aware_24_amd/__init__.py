@@ -29,6 +29,7 @@ FA2_ERR_ALIGN = -5
 FA2_ERR_ALIAS = -6
 FA2_ERR_HIP = -7
 FA2_ERR_WORKSPACE = -8
+FA2_ERR_DEVICE = -9
 NOALLOC_WORKSPACE_BYTES = 32 << 20  # FA2_NOALLOC_WORKSPACE_BYTES
 
 # Every symbol include/fa2.h declares.

@@ -165,6 +165,20 @@ fa2::BwdArgs make_bwd_args(const void *q, const void *k, const void *v,
 
 int finish(hipError_t e) { return e == hipSuccess ? FA2_OK : FA2_ERR_HIP; }
 
+// A stream, when given, must belong to the current device: the kernels run
+// on the stream's device and address the caller's buffers (and, for the
+// allocation-free entry point, the static array) of the current one.
+int check_stream(void *stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // the null stream and HIP's implicit default streams are the current device's
+  if (st == nullptr || st == hipStreamLegacy || st == hipStreamPerThread) return FA2_OK;
+  int cur = -1;
+  hipDevice_t sdev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return FA2_ERR_HIP;
+  if (hipStreamGetDevice(st, &sdev) != hipSuccess) return FA2_ERR_HIP;
+  return sdev == cur ? FA2_OK : FA2_ERR_DEVICE;
+}
+
 }  // namespace
 
 FA2_EXPORT int fa2_fwd(const void *q, const void *k, const void *v, void *o,
@@ -172,6 +186,7 @@ FA2_EXPORT int fa2_fwd(const void *q, const void *k, const void *v, void *o,
                        int causal, void *stream) {
   int rc = validate(q, k, v, o, lse, B, H, H, N, N, d, scale, 2, 2,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc == FA2_OK) rc = check_stream(stream);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
       make_args(q, k, v, o, lse, B, H, H, N, N, d, scale, causal), false,
@@ -183,6 +198,7 @@ FA2_EXPORT int fa2_fwd_gqa(const void *q, const void *k, const void *v,
                            int d, float scale, int causal, void *stream) {
   int rc = validate(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, 2, 2,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc == FA2_OK) rc = check_stream(stream);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
       make_args(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, causal), false,
@@ -195,6 +211,7 @@ FA2_EXPORT int fa2_fwd_gqa_o32(const void *q, const void *k, const void *v,
                                void *stream) {
   int rc = validate(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, 2, 4,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc == FA2_OK) rc = check_stream(stream);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
       make_args(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, causal), true,
@@ -206,6 +223,7 @@ FA2_EXPORT int fa2_fwd_o32(const void *q, const void *k, const void *v,
                            float scale, int causal, void *stream) {
   int rc = validate(q, k, v, o, lse, B, H, H, N, N, d, scale, 2, 4,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
+  if (rc == FA2_OK) rc = check_stream(stream);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_bf16(
       make_args(q, k, v, o, lse, B, H, H, N, N, d, scale, causal), true,
@@ -242,6 +260,8 @@ static int splitkv(const void *q, const void *k, const void *v, void *o, float *
       for (const Range &x : others)
         if (overlaps(p, x)) return FA2_ERR_ALIAS;
   }
+  rc = check_stream(stream);
+  if (rc != FA2_OK) return rc;
   fa2::FwdArgs a = make_args(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal);
   a.n_splits = n_splits;
   a.o_part = o_part;
@@ -285,15 +305,18 @@ FA2_EXPORT int fa2_fwd_splitkv_noalloc(const void *q, const void *k,
   const int64_t blocks = bh * ((static_cast<int64_t>(Nq) + fa2::kBf16RowsPerBlock - 1) /
                                fa2::kBf16RowsPerBlock);
   if (blocks * n_splits > INT32_MAX) return FA2_ERR_SHAPE;
+  // [n_splits][B*H][Nq][d] fp32 partial outputs, then [n_splits][B*H][Nq]
+  // fp32 partial lse (the first part is a multiple of 256 bytes: d >= 64)
+  const int64_t o_floats = static_cast<int64_t>(n_splits) * bh * Nq * d;
+  const int64_t l_floats = static_cast<int64_t>(n_splits) * bh * Nq;
+  if (n_splits > 1 &&
+      (o_floats + l_floats) * 4 > static_cast<int64_t>(FA2_NOALLOC_WORKSPACE_BYTES))
+    return FA2_ERR_WORKSPACE;
+  rc = check_stream(stream);
+  if (rc != FA2_OK) return rc;
   fa2::FwdArgs a = make_args(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal);
   a.n_splits = n_splits;
   if (n_splits > 1) {
-    // [n_splits][B*H][Nq][d] fp32 partial outputs, then [n_splits][B*H][Nq]
-    // fp32 partial lse (the first part is a multiple of 256 bytes: d >= 64)
-    const int64_t o_floats = static_cast<int64_t>(n_splits) * bh * Nq * d;
-    const int64_t l_floats = static_cast<int64_t>(n_splits) * bh * Nq;
-    if ((o_floats + l_floats) * 4 > static_cast<int64_t>(FA2_NOALLOC_WORKSPACE_BYTES))
-      return FA2_ERR_WORKSPACE;
     float *ws = nullptr;
     if (fa2::fwd_scratch(&ws) != hipSuccess) return FA2_ERR_HIP;
     a.o_part = ws;
@@ -322,6 +345,8 @@ FA2_EXPORT int fa2_quantize_fp8(const void *x, void *codes, int *exps, int B,
   if (overlaps(rc, rx) || overlaps(rc, re) || overlaps(rc, rs) ||
       overlaps(re, rx) || overlaps(re, rs))
     return FA2_ERR_ALIAS;
+  const int rc_stream = check_stream(stream);
+  if (rc_stream != FA2_OK) return rc_stream;
   fa2::QuantArgs a;
   a.x = x;
   a.codes = codes;
@@ -354,6 +379,8 @@ static int fwd_fp8(const void *q8, const int *qe, const void *k8, const int *ke,
   for (const Range &r : out)
     for (const Range &e : ex)
       if (overlaps(r, e)) return FA2_ERR_ALIAS;
+  rc = check_stream(stream);
+  if (rc != FA2_OK) return rc;
   fa2::Fp8Args a;
   a.q = q8;
   a.k = k8;
@@ -393,6 +420,7 @@ FA2_EXPORT int fa2_fwd_fp32(const float *q, const float *k, const float *v,
                             float scale, int causal, void *stream) {
   int rc = validate(q, k, v, o, lse, B, H, H, N, N, d, scale, 4, 4,
                     fa2::kFp32RowsPerBlock, INT32_MAX);
+  if (rc == FA2_OK) rc = check_stream(stream);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_fwd_fp32(
       make_args(q, k, v, o, lse, B, H, H, N, N, d, scale, causal),
@@ -406,6 +434,7 @@ static int bwd(const void *q, const void *k, const void *v, const void *o,
                bool o32, void *stream) {
   int rc = validate_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv,
                         N, d, scale, o32 ? 4 : 2, n_gsplits, dkv_part);
+  if (rc == FA2_OK) rc = check_stream(stream);
   if (rc != FA2_OK) return rc;
   return finish(fa2::launch_bwd_bf16(
       make_bwd_args(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d,
@@ -462,6 +491,8 @@ FA2_EXPORT const char *fa2_strerror(int code) {
     case FA2_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FA2_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA2_ERR_HIP: return "HIP kernel launch failed";
+    case FA2_ERR_DEVICE:
+      return "the stream belongs to another device than the current HIP device";
     case FA2_ERR_WORKSPACE:
       return "the key-range partials exceed the library's static workspace "
              "(FA2_NOALLOC_WORKSPACE_BYTES)";
@@ -469,4 +500,4 @@ FA2_EXPORT const char *fa2_strerror(int code) {
   }
 }
 
-FA2_EXPORT int fa2_version(void) { return 7; }
+FA2_EXPORT int fa2_version(void) { return 8; }

@@ -34,7 +34,9 @@
  * what the HIP runtime caches and one static device array per GPU (the
  * workspace of fa2_fwd_splitkv_noalloc, FA2_NOALLOC_WORKSPACE_BYTES, held
  * until the process ends).  All pointers are device pointers (hipMalloc
- * or equivalent) of the current HIP device.  Calls are thread-safe.
+ * or equivalent) of the current HIP device, and a stream other than NULL and
+ * HIP's legacy and per-thread default streams must be a stream of that
+ * device (FA2_ERR_DEVICE otherwise).  Calls are thread-safe.
  *
  * Asynchrony: every entry point enqueues its kernel on `stream` (a
  * hipStream_t; NULL means the null stream) and returns without waiting.
@@ -47,8 +49,9 @@
  * and lse; dq, dk, dv and delta of the backward pass) must not overlap any
  * input or each other (FA2_ERR_ALIAS).
  *
- * Errors: every argument is validated on the host before any HIP call, so a
- * rejected call has no effect and enqueues nothing.  A non-zero return is
+ * Errors: every argument is validated on the host before anything is
+ * enqueued (the only HIP calls before that query the current device and the
+ * stream's device), so a rejected call has no effect and enqueues nothing.  A non-zero return is
  * one of the FA2_ERR_* codes below; fa2_strerror() names it.
  */
 #ifndef FA2_H
@@ -69,6 +72,8 @@ extern "C" {
 #define FA2_ERR_HIP (-7)     /* the kernel launch failed (hipGetLastError)     */
 #define FA2_ERR_WORKSPACE (-8) /* fa2_fwd_splitkv_noalloc: the partials need
                                   more than FA2_NOALLOC_WORKSPACE_BYTES      */
+#define FA2_ERR_DEVICE (-9)  /* the stream belongs to another device than the
+                                current HIP device                            */
 
 /* Size limits (FA2_ERR_SHAPE beyond them): B*H*N*d <= FA2_MAX_ELEMS elements
    per tensor (2^40, far above one GPU's memory); B*H and the number of
@@ -322,9 +327,10 @@ int fa2_bwd_gqa_o32(const void *q, const void *k, const void *v,
 /* Static English description of a return code (never NULL). */
 const char *fa2_strerror(int code);
 
-/* Library ABI version: 7 (2 added the backward pass, 3 grouped K/V heads,
+/* Library ABI version: 8 (2 added the backward pass, 3 grouped K/V heads,
    4 split key ranges with separate query and key lengths, 5 the FP8 path,
-   6 the grouped-head backward, 7 fa2_fwd_splitkv_noalloc). */
+   6 the grouped-head backward, 7 fa2_fwd_splitkv_noalloc, 8 FA2_ERR_DEVICE
+   for a stream of another device). */
 int fa2_version(void);
 
 #ifdef __cplusplus

@@ -16,7 +16,19 @@ namespace {
 int g_launches = 0;
 hipError_t g_result = hipSuccess;
 alignas(256) float g_scratch[64];
+int g_cur_device = 0;         // what hipGetDevice reports
+int g_stream_device = 0;      // what hipStreamGetDevice reports for any stream
+hipError_t g_query = hipSuccess;
 }  // namespace
+
+hipError_t hipGetDevice(int *device) {
+  *device = g_cur_device;
+  return g_query;
+}
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t *device) {
+  *device = g_stream_device;
+  return g_query;
+}
 
 namespace fa2 {
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool, hipStream_t) {
@@ -144,6 +156,38 @@ int main() {
                      0.1f, 1, 5, F(10), nullptr), FA2_ERR_SHAPE);
   EXPECT(fa2_bwd_gqa(P(0), P(1), P(2), P(3), P(4), F(5), F(6), P(7), P(8), P(9), 2, 8, 2, 300, 128,
                      0.1f, 1, 4, nullptr, nullptr), FA2_ERR_NULL);
+  // a stream must belong to the current device; the null stream always does
+  {
+    hipStream_t st = reinterpret_cast<hipStream_t>(P(20));
+    EXPECT(fa2_fwd(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, st), FA2_OK);
+    g_stream_device = 1;
+    EXPECT(fa2_fwd(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, st), FA2_ERR_DEVICE);
+    EXPECT(fa2_fwd(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, nullptr), FA2_OK);
+    EXPECT(fa2_fwd(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, hipStreamPerThread),
+           FA2_OK);
+    EXPECT(fa2_fwd(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, hipStreamLegacy), FA2_OK);
+    EXPECT(fa2_fwd_gqa(P(0), P(1), P(2), P(3), F(4), 2, 8, 2, 300, 128, 0.1f, 1, st),
+           FA2_ERR_DEVICE);
+    EXPECT(fa2_fwd_splitkv(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1, 4, F(5),
+                           F(6), st), FA2_ERR_DEVICE);
+    EXPECT(fa2_fwd_splitkv_noalloc(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1,
+                                   4, st), FA2_ERR_DEVICE);
+    EXPECT(fa2_fwd_fp32(F(0), F(1), F(2), F(3), F(4), 1, 1, 128, 64, 0.125f, 0, st),
+           FA2_ERR_DEVICE);
+    EXPECT(fa2_quantize_fp8(P(0), P(1), static_cast<int *>(P(2)), 1, 2, 100, 128, 64, F(6), st),
+           FA2_ERR_DEVICE);
+    EXPECT(fa2_fwd_fp8(P(0), static_cast<int *>(P(1)), P(2), static_cast<int *>(P(3)), P(4),
+                       static_cast<int *>(P(5)), P(6), F(7), 1, 2, 100, 128, 0.1f, 1, 1, st),
+           FA2_ERR_DEVICE);
+    EXPECT(fa2_bwd(P(0), P(1), P(2), P(3), P(4), F(5), F(6), P(7), P(8), P(9), 1, 2, 200, 128,
+                   0.1f, 1, st), FA2_ERR_DEVICE);
+    // argument errors come first
+    EXPECT(fa2_fwd(nullptr, P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, st), FA2_ERR_NULL);
+    g_stream_device = 0;
+    g_query = hipErrorInvalidValue;  // a failing query is a HIP error
+    EXPECT(fa2_fwd(P(0), P(1), P(2), P(3), F(4), 1, 2, 64, 64, 0.125f, 0, st), FA2_ERR_HIP);
+    g_query = hipSuccess;
+  }
   // a failing launch is reported as FA2_ERR_HIP
   g_result = hipErrorLaunchFailure;
   {
@@ -157,7 +201,8 @@ int main() {
   g_result = hipSuccess;
   // every code has its own message; unknown codes too
   const int codes[] = {FA2_OK, FA2_ERR_NULL, FA2_ERR_SHAPE, FA2_ERR_HEADDIM, FA2_ERR_SCALE,
-                       FA2_ERR_ALIGN, FA2_ERR_ALIAS, FA2_ERR_HIP, FA2_ERR_WORKSPACE, 12345, -99};
+                       FA2_ERR_ALIGN, FA2_ERR_ALIAS, FA2_ERR_HIP, FA2_ERR_WORKSPACE,
+                       FA2_ERR_DEVICE, 12345, -99};
   for (int c : codes) {
     const char *m = fa2_strerror(c);
     if (!m || !std::strlen(m)) {
@@ -165,7 +210,7 @@ int main() {
       ++g_fail;
     }
   }
-  if (fa2_version() != 7) {
+  if (fa2_version() != 8) {
     std::printf("FAIL: version %d\n", fa2_version());
     ++g_fail;
   }

@@ -13,3 +13,9 @@ enum {
   hipErrorLaunchFailure = 719
 };
 typedef struct ihipStream_t *hipStream_t;
+typedef int hipDevice_t;
+#define hipStreamLegacy ((hipStream_t)1)
+#define hipStreamPerThread ((hipStream_t)2)
+/* defined by the driver, which decides what they report */
+hipError_t hipGetDevice(int *device);
+hipError_t hipStreamGetDevice(hipStream_t stream, hipDevice_t *device);

@@ -50,7 +50,7 @@ def test_codes_match_header():
 
 
 def test_version_and_strerror(L):
-    assert fa2.version() == 7
+    assert fa2.version() == 8
     seen = set()
     for name, code in header_codes().items():
         msg = fa2.strerror(code)
