@@ -58,7 +58,7 @@ def kv_ref(k, v, H):
     return oracle.expand_kv_heads(k, H), oracle.expand_kv_heads(v, H)
 
 
-FWD = draws("fwd", 24, 2026)
+FWD = draws("fwd", 96, 2026)
 
 
 @pytest.mark.parametrize("case", FWD, ids=["fwd%d" % c[1] for c in FWD])
@@ -80,7 +80,7 @@ def test_forward_random(fa2, case):
     assert res["ok"], parity.describe(res)
 
 
-SPLIT = draws("split", 16, 2027)
+SPLIT = draws("split", 48, 2027)
 
 
 @pytest.mark.parametrize("case", SPLIT, ids=["split%d" % c[1] for c in SPLIT])
@@ -108,7 +108,7 @@ def test_splitkv_random(fa2, case):
     assert res["ok"], parity.describe(res)
 
 
-BWD = [c for c in draws("bwd", 16, 2028)]
+BWD = [c for c in draws("bwd", 32, 2028)]
 
 
 @pytest.mark.parametrize("case", BWD, ids=["bwd%d" % c[1] for c in BWD])
