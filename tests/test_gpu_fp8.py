@@ -144,3 +144,48 @@ def test_fp8_full_size_headline(fa2):
     for h in range(w.B * w.H):
         rs = parity.compare_fp8(oh[h], rh[h])
         assert rs["rel_l2"] <= parity.FP8_REL_L2 and rs["max_rel"] <= parity.FP8_MAX_REL, (h, rs)
+
+
+def fp8_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        N = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 700)),
+                            int(rng.integers(700, 1600))]))
+        out.append((i, int(rng.integers(1, 3)), int(rng.integers(1, 4)), N, d,
+                    bool(rng.integers(0, 2)),
+                    float(rng.choice([1.0 / math.sqrt(d), rng.uniform(-0.2, 0.2)])),
+                    bool(rng.integers(0, 2)), int(rng.choice([64, 128])),
+                    int(rng.integers(0, 1 << 30))))
+    return out
+
+
+FP8_RANDOM = fp8_draws(32, 2030)
+
+
+@pytest.mark.parametrize("case", FP8_RANDOM, ids=["fp8r%d" % c[0] for c in FP8_RANDOM])
+def test_fp8_random(fa2, case):
+    """Seeded random shapes, masks, scales, rotations and quantiser block
+    heights: codes and exponents bit for bit, attention against the
+    dequantised oracle as above."""
+    import torch
+    i, B, H, N, d, causal, scale, rot, rows, seed = case
+    q, k, v = wl.make_inputs(B, H, N, d, "bf16", seed=seed)
+    sg = wl.make_signs(d) if rot else None
+    dev = torch.device("cuda:0")
+    say("fp8 random B=%d H=%d N=%d d=%d causal=%s scale=%.4f rotate=%s rows=%d"
+        % (B, H, N, d, causal, scale, rot, rows))
+    codes, exps = fa2.quantize_fp8(q.to(dev), rows, sg.to(dev) if sg is not None else None)
+    torch.cuda.synchronize()
+    c_ref, e_ref = oracle.quantize_fp8(q, rows, sg.numpy() if sg is not None else None)
+    assert np.array_equal(exps.cpu().numpy(), e_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    o_ref, l_ref, _ = oracle.attention_fp8_reference(
+        q, k, v, scale, causal, sg.numpy() if sg is not None else None)
+    odt = torch.float32 if i % 2 else torch.bfloat16
+    o, lse = run_fp8(fa2, q, k, v, causal, sg, odt, scale)
+    res = parity.compare_fp8(parity.to_np(o), o_ref)
+    assert res["finite"] and res["rel_l2"] <= parity.FP8_REL_L2 \
+        and res["max_rel"] <= parity.FP8_MAX_REL, res
+    assert np.max(np.abs(parity.to_np(lse) - l_ref)) <= 1e-2
