@@ -33,7 +33,10 @@
 // head of one range of the group in turn, accumulating in the same
 // registers; with one range per group it writes dK/dV directly, with several
 // each range writes an fp32 partial and reduce_parts_kernel adds the
-// partials in range order (deterministic, no atomics).
+// partials in range order (deterministic, no atomics).  Causal with several
+// heads per range, dkdv_pair_kernel does the same for two key blocks per
+// workgroup, ordered so that a range's workgroups read the same query tiles
+// at the same time (see there).
 //
 // MFMA layouts (v_mfma_f32_32x32x16_bf16): A lane l holds A[l%32][8(l/32)
 // .. +7], B lane l holds B[8(l/32) .. +7][l%32], the result register r of
@@ -77,7 +80,8 @@ struct BwdParams {
   int n;          // sequence length
   int n_blocks;   // ceil(n / 128)
   int total;      // B*H*n_blocks (dq grid size)
-  int total_kv;   // B*H_kv*n_gsplits*n_blocks (dkdv grid size)
+  int total_kv;   // dkdv grid size: B*H_kv*n_gsplits*n_blocks, or with
+                  // paired key blocks B*H_kv*n_gsplits*ceil(n_blocks / 2)
   int h;          // query heads per batch index
   int group;      // query heads per K/V head
   int n_gsplits;  // ranges of a group's query heads
@@ -263,6 +267,66 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t *o,
 
 // ---- dK, dV -----------------------------------------------------------------
 //
+// One step of the dK/dV accumulation: the tile of 64 queries (Q, dO, lse in
+// base-2 units, D) in LDS at qb/ob/lb/db against this wave's 32 keys
+// (k0 + 32w .. +31, K and V in registers), as two 32-query halves:
+//   S  = Q K^T      A = Q rows (LDS),  B = K (registers)  -> lane = key
+//   dP = dO V^T     A = dO rows (LDS), B = V (registers)
+//   P = exp2(S c - lse log2 e), dS = P (dP - D)
+//   dV^T += dO^T P  A = dO columns (transposed LDS reads), B = P (bf16)
+//   dK^T += Q^T dS  A = Q columns,                        B = dS (bf16)
+// MASKED: the tile holds a query before one of the block's keys (causal) --
+// a compile-time switch, so that the other tiles carry no mask
+// instructions.  A wave whose keys all come after every query of the tile
+// has nothing to do.
+template <int D, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void dkdv_tile(const char *qb, const char *ob,
+                                          const char *lb, const char *db,
+                                          const TileOffsets<D> &off,
+                                          const bf16x8 (&kreg)[D / 16],
+                                          const bf16x8 (&vreg)[D / 16],
+                                          f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32],
+                                          float c, int t, int kw, int kj, int hh) {
+  using C = BCfg<D>;
+  if (CAUSAL && t * kTileRows + kTileRows - 1 < kw) return;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {  // 32-query halves of the tile
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::NDT; ++ks) {
+      s = mfma(row_operand<D>(qb, off, 32 * h, ks), kreg[ks], s);
+      dp = mfma(row_operand<D>(ob, off, 32 * h, ks), vreg[ks], dp);
+    }
+    // register r holds query 32h + 8(r/4) + 4hh + r%4 of the tile
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int qrow = 32 * h + 8 * a + 4 * hh;
+      const f32x4 l4 = lds_load<f32x4>(lb, qrow * 4);  // lse log2(e)
+      const f32x4 d4 = lds_load<f32x4>(db, qrow * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * a + e;
+        float x = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
+        if (MASKED && kj > t * kTileRows + qrow + e) x = 0.f;
+        const float ds = x * (dp[r] - d4[e]);
+        pb[r >> 3][r & 7] = static_cast<__bf16>(x);
+        sb[r >> 3][r & 7] = static_cast<__bf16>(ds);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct) {
+        dv[ct] = mfma(col_operand<D>(ob, off, ct, 2 * h + u), pb[u], dv[ct]);
+        dk[ct] = mfma(col_operand<D>(qb, off, ct, 2 * h + u), sb[u], dk[ct]);
+      }
+  }
+}
+
+//
 // Workgroup: 128 keys of one K/V head, wave w owns keys k0 + 32w + lane%32,
 // and one range of the query heads that read this K/V head (all of them, or
 // one of n_gsplits ranges).  K and V of those keys are B operands held in
@@ -275,7 +339,9 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(const uint16_t *o,
 //   dK^T += Q^T dS  A = Q columns,                        B = dS (bf16)
 // The lse and D values of a tile are staged in LDS next to it (rows past
 // the sequence end read as 0, which gives them zero weight because their
-// Q and dO rows are zero too).
+// Q and dO rows are zero too).  (The tile step is written out here rather
+// than called as dkdv_tile: through the function the register allocator
+// placed a spill in the unmasked tile loop of the causal d = 128 variants.)
 template <int D, bool CAUSAL, bool O32, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
   using C = BCfg<D>;
@@ -459,6 +525,146 @@ __global__ __launch_bounds__(kThreads, 2) void dkdv_kernel(BwdParams p) {
   }
 }
 
+// Causal dK/dV with grouped K/V heads (a range of several query heads per
+// workgroup): each workgroup takes key blocks j and n_blocks - 1 - j in
+// turn, which together span the same number of query tiles for every j, so
+// the n_blocks / 2 workgroups of a (K/V head, head range) start together
+// and end together.  The first block is walked downward from the last
+// query tile to its diagonal, the second upward from its diagonal to the
+// last tile, the range's heads interleaved at each tile: at the workgroups'
+// s-th tile step every first block is at tile nt - 1 - s and every second
+// block at tile s - 2, so a unit reads two tiles per head at a time, whose
+// Q and dO are fetched once and stay in L2 while all of them read it (one
+// block per workgroup, the blocks that start as slots free up each stream
+// the range's Q and dO on their own).  The tile steps are dkdv_tile's.
+template <int D, bool O32>
+__global__ __launch_bounds__(kThreads, 2) void dkdv_pair_kernel(BwdParams p) {
+  using C = BCfg<D>;
+  // [Q 0][Q 1][dO 0][dO 1][lse 0][lse 1][D 0][D 1], as in dkdv_kernel
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE_BYTES + 4 * 1024];
+  auto qbuf = [&](int i) { return smem + i * C::TILE_BYTES; };
+  auto obuf = [&](int i) { return smem + (2 + i) * C::TILE_BYTES; };
+  auto lbuf = [&](int i) { return smem + 4 * C::TILE_BYTES + i * 1024; };
+  auto dbuf = [&](int i) { return smem + 4 * C::TILE_BYTES + (2 + i) * 1024; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, hh = lane >> 5;
+
+  const int pairs = (p.n_blocks + 1) / 2;
+  const int logical = xcd_remap(blockIdx.x, p.total_kv);
+  const int unit = logical / pairs;             // (K/V head, query-head range)
+  const int jb = logical - unit * pairs;
+  const int kvbh = unit / p.n_gsplits;
+  const int gs = unit - kvbh * p.n_gsplits;
+  const int hkv = p.h / p.group;
+  const int g_lo = gs * p.group / p.n_gsplits;
+  const int ng = (gs + 1) * p.group / p.n_gsplits - g_lo;  // >= 1
+  const int qbh0 = (kvbh / hkv) * p.h + (kvbh % hkv) * p.group + g_lo;
+  const int N = p.n;
+  const size_t head = static_cast<size_t>(kvbh) * N * D;
+  const int head_bytes = N * D * 2;
+  const TileOffsets<D> off = tile_offsets<D>(lane, wv);
+  const int st_off = lane < 16 ? lane * 16 : 0x7ffffff0;
+  const int nt = (N + kTileRows - 1) / kTileRows;
+
+  auto issue = [&](int g, int t, int buf) {
+    const size_t rows = static_cast<size_t>(qbh0 + g) * N;
+    issue_tile<D>(p.q + rows * D, head_bytes, off, qbuf(buf), wv, t * kTileRows);
+    issue_tile<D>(p.dout + rows * D, head_bytes, off, obuf(buf), wv, t * kTileRows);
+    if (wv == 0)
+      dma16(tile_desc(p.lse + rows, N * 4, t * kTileRows * 4), st_off, 0,
+            lds_addr(lbuf(buf)));
+    if (wv == 1)
+      dma16(tile_desc(p.delta + rows, N * 4, t * kTileRows * 4), st_off, 0,
+            lds_addr(dbuf(buf)));
+  };
+  if (N % kTileRows != 0) {
+    for (int i = tid; i < (4 * C::TILE_BYTES + 4 * 1024) / 16; i += kThreads)
+      reinterpret_cast<u32x4 *>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+  auto lse_to_base2 = [&](int buf) {
+    if (wv == 0) {
+      float *l = reinterpret_cast<float *>(lbuf(buf)) + lane;
+      *l = *l * kLog2e;
+    }
+  };
+  const float c = p.c;
+  int b = 0;  // LDS buffer of the current step
+
+  auto run_block = [&](auto down_tag, int kb) {
+    constexpr bool down = decltype(down_tag)::value;
+    const int k0 = kb * kBlk;
+    const int kw = k0 + 32 * wv;
+    const int kj = kw + lr;
+    bf16x8 kreg[C::NDT], vreg[C::NDT];
+    load_row_operand<D>(p.k + head, head_bytes, kj, hh, kreg);
+    load_row_operand<D>(p.v + head, head_bytes, kj, hh, vreg);
+    f32x16 dk[C::NCT], dv[C::NCT];
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dk[ct][r] = dv[ct][r] = 0.f;
+    const int t0 = k0 / kTileRows;
+    const int t_mask_end = min((k0 + kBlk - 1 + kTileRows - 1) / kTileRows, nt);
+
+    // step (g, t), the next one (gn, tn) prefetched into the other buffer
+    auto step = [&](auto masked_tag, int g, int t, int gn, int tn) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      if (gn >= 0) issue(gn, tn, b ^ 1);
+      dkdv_tile<D, true, MASKED>(qbuf(b), obuf(b), lbuf(b), dbuf(b), off, kreg, vreg, dk,
+                                 dv, c, t, kw, kj, hh);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (gn >= 0) lse_to_base2(b ^ 1);
+      __syncthreads();
+      b ^= 1;
+    };
+    // tiles lo .. hi in the walk's direction, each with the range's heads
+    constexpr int dt = down ? -1 : 1;
+    const int t_last = down ? t0 : nt - 1;
+    auto walk = [&](auto masked_tag, int lo, int hi) {
+      if (lo > hi) return;
+      const int t_end = down ? lo : hi;
+      for (int t = down ? hi : lo;; t += dt) {
+        for (int g = 0; g < ng; ++g) {
+          const bool lg = g + 1 == ng;
+          const int gn = !lg ? g + 1 : (t != t_last ? 0 : -1);
+          step(masked_tag, g, t, gn, lg ? t + dt : t);
+        }
+        if (t == t_end) break;
+      }
+    };
+    // this block's first step, into the current buffer (free: the previous
+    // block's last step prefetched nothing and ended with a barrier)
+    issue(0, down ? nt - 1 : t0, b);
+    __builtin_amdgcn_s_waitcnt(0);
+    lse_to_base2(b);
+    __syncthreads();
+    if constexpr (down) {
+      walk(std::false_type{}, t_mask_end, nt - 1);
+      walk(std::true_type{}, t0, t_mask_end - 1);
+    } else {
+      walk(std::true_type{}, t0, t_mask_end - 1);
+      walk(std::false_type{}, t_mask_end, nt - 1);
+    }
+    if (kj < N) {
+      const size_t row = head + static_cast<size_t>(kj) * D;
+      if (p.n_gsplits == 1) {
+        store_rows<D, O32>(p.dk, row, hh, dk, p.scale);
+        store_rows<D, O32>(p.dv, row, hh, dv, 1.0f);
+      } else {
+        const size_t pofs = static_cast<size_t>(gs) * p.part_stride;
+        store_rows<D, true>(p.dk_part + pofs, row, hh, dk, p.scale);
+        store_rows<D, true>(p.dv_part + pofs, row, hh, dv, 1.0f);
+      }
+    }
+  };
+  run_block(std::true_type{}, jb);
+  if (2 * jb + 1 != p.n_blocks) run_block(std::false_type{}, p.n_blocks - 1 - jb);
+}
+
 // dK or dV from the fp32 partials of the n_gsplits query-head ranges:
 // out[e] = sum over s of part[s][e], in increasing s.
 template <bool O32>
@@ -612,7 +818,10 @@ hipError_t launch(const BwdParams &prm, int64_t rows, hipStream_t s) {
                      0, s, prm.o, prm.dout, prm.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (prm.group > prm.n_gsplits)  // some range holds several query heads
+  if (CAUSAL && prm.group > prm.n_gsplits)  // paired blocks, several heads per range
+    hipLaunchKernelGGL((dkdv_pair_kernel<D, O32>), dim3(prm.total_kv), dim3(kThreads), 0, s,
+                       prm);
+  else if (prm.group > prm.n_gsplits)  // some range holds several query heads
     hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, O32, true>), dim3(prm.total_kv),
                        dim3(kThreads), 0, s, prm);
   else
@@ -664,7 +873,11 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, bool o32, hipStream_t s) {
   prm.h = a.h;
   prm.group = a.group;
   prm.n_gsplits = a.n_gsplits;
-  prm.total_kv = a.bh / a.group * a.n_gsplits * prm.n_blocks;
+  // causal with several query heads per range: dkdv_pair_kernel, one
+  // workgroup per pair of key blocks
+  const bool paired = a.causal && a.group > a.n_gsplits;
+  prm.total_kv = a.bh / a.group * a.n_gsplits *
+                 (paired ? (prm.n_blocks + 1) / 2 : prm.n_blocks);
   prm.part_stride = static_cast<size_t>(a.bh / a.group) * a.n * a.d;
   prm.dk_part = a.dkv_part;
   prm.dv_part = a.dkv_part ? a.dkv_part + static_cast<size_t>(a.n_gsplits) * prm.part_stride
