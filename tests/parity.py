@@ -1,6 +1,6 @@
 """Comparison of the HIP library's outputs with the fp64 oracle.
 
-Tolerances (bf16 inputs; the benchmark spec's max-abs 1e-2 and rel-L2 5e-3):
+Tolerances (bf16 inputs; the stated bounds are max-abs 1e-2 and rel-L2 5e-3):
 * fp32 output (fa2_fwd_o32): max |O - O_ref| <= 1e-2 and
   ||O - O_ref||_2 / ||O_ref||_2 <= 5e-3, literally;
 * bf16 output (fa2_fwd): max |O - O_ref| <= 1e-2 literally (``literal=True``)
