@@ -54,9 +54,15 @@ __device__ __forceinline__ int block_exponent(float amax) {
 }
 
 // Four floats to four e4m3 codes, byte i = code of x_i (round to nearest
-// even; the magnitudes here never exceed 448).
+// even; the magnitudes here never exceed 448).  The first conversion writes
+// the low half-word and the second the high one, so the register's prior
+// contents never reach the result: it starts from whatever the register
+// holds (an empty asm that only claims to define it, tied to x0 so that
+// every call gets its own) rather than from a zero that costs a move.
 __device__ __forceinline__ int cvt_fp8x4(float x0, float x1, float x2, float x3) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  int any;
+  asm("; fp8 pack start" : "=v"(any) : "v"(x0));
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, any, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, lo, true);
 }
 
