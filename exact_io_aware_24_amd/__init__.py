@@ -142,6 +142,26 @@ def _check_tensors(q, k, v, grouped=False):
         raise ValueError("q, k, v are on different devices")
 
 
+def _buffer(t, name, shape, dtype, device, workspace=False):
+    """An output or workspace tensor: allocated when ``t`` is None, else
+    checked to be a contiguous ``dtype`` GPU tensor on ``device`` of exactly
+    ``shape`` (``workspace``: of at least that many elements, any shape).
+    The kernels write every element the shape implies, so a smaller buffer
+    must never reach them."""
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    need = math.prod(shape)
+    ok = (isinstance(t, torch.Tensor) and t.is_cuda and t.device == device
+          and t.dtype == dtype and t.is_contiguous()
+          and (t.numel() >= need if workspace else tuple(t.shape) == tuple(shape)))
+    if not ok:
+        what = ("at least %d elements" % need) if workspace else "shape %s" % (tuple(shape),)
+        raise ValueError("%s must be a contiguous %s tensor on %s with %s"
+                         % (name, dtype, device, what))
+    return t
+
+
 def forward(q, k, v, causal: bool = False, scale: float | None = None,
             out_dtype=None, out=None, lse=None, return_lse: bool = True):
     """Exact attention forward: ``softmax(scale * q k^T [+ causal mask]) v``.
@@ -180,19 +200,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
             raise ValueError("out_dtype must be bfloat16 or float32")
         if H_kv != H:
             fn = fn.replace("fa2_fwd", "fa2_fwd_gqa")
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
-    elif out.shape != q.shape or out.dtype != odt or not out.is_contiguous() \
-            or out.device != q.device:
-        raise ValueError("out must be a contiguous %s tensor shaped like q" % odt)
-    if return_lse:
-        if lse is None:
-            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-        elif lse.shape != (B, H, N) or lse.dtype != torch.float32 \
-                or not lse.is_contiguous() or lse.device != q.device:
-            raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    else:
-        lse = None
+    out = _buffer(out, "out", (B, H, N, d), odt, q.device)
+    lse = _buffer(lse, "lse", (B, H, N), torch.float32, q.device) if return_lse else None
     heads = (B, H, H_kv) if H_kv != H else (B, H)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -314,7 +323,7 @@ def default_splits(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
     compute unit, twice over) while keeping every range at least four key
     tiles long."""
     blocks = B * H * ((Nq + 127) // 128)
-    tile = 64 if d == 128 else 128
+    tile = 64  # keys per tile of the bf16 kernels, d = 64 and d = 128 alike
     tiles = (Nk + tile - 1) // tile
     n = -(-1024 // blocks)
     return int(max(1, min(n, tiles // 4, MAX_SPLITS)))
@@ -349,17 +358,13 @@ def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     if fn is None:
         raise ValueError("out_dtype must be bfloat16 or float32")
     dev = q.device
-    if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=odt, device=dev)
-    if return_lse and lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
-    if not return_lse:
-        lse = None
+    out = _buffer(out, "out", (B, H, Nq, d), odt, dev)
+    lse = _buffer(lse, "lse", (B, H, Nq), torch.float32, dev) if return_lse else None
     if n_splits > 1:
-        if o_part is None:
-            o_part = torch.empty((n_splits, B, H, Nq, d), dtype=torch.float32, device=dev)
-        if lse_part is None:
-            lse_part = torch.empty((n_splits, B, H, Nq), dtype=torch.float32, device=dev)
+        o_part = _buffer(o_part, "o_part", (n_splits, B, H, Nq, d), torch.float32, dev,
+                         workspace=True)
+        lse_part = _buffer(lse_part, "lse_part", (n_splits, B, H, Nq), torch.float32, dev,
+                           workspace=True)
     ptr = lambda t: t.data_ptr() if t is not None else None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
@@ -394,12 +399,8 @@ def forward_splitkv_noalloc(q, k, v, causal: bool = False,
     if n_splits is None:
         n_splits = default_splits(B, H, Nq, Nk, d)
     dev = q.device
-    if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=dev)
-    if return_lse and lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
-    if not return_lse:
-        lse = None
+    out = _buffer(out, "out", (B, H, Nq, d), torch.bfloat16, dev)
+    lse = _buffer(lse, "lse", (B, H, Nq), torch.float32, dev) if return_lse else None
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         rc = lib().fa2_fwd_splitkv_noalloc(
@@ -432,14 +433,17 @@ def quantize_fp8(x, block_rows: int, signs=None, codes=None, exps=None):
             or not x.is_contiguous() or x.dtype != torch.bfloat16:
         raise ValueError("x must be a contiguous bfloat16 GPU tensor [B, H, N, d]")
     B, H, N, d = (int(v) for v in x.shape)
+    if block_rows not in (64, 128):
+        raise ValueError("block_rows must be 64 or 128")
     nb = -(-N // block_rows)
-    if codes is None:
-        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    if exps is None:
-        exps = torch.empty((B, H, nb), dtype=torch.int32, device=x.device)
-    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != d
-                              or not signs.is_cuda):
-        raise ValueError("signs must be a float32 GPU tensor of d values")
+    codes = _buffer(codes, "codes", (B, H, N, d), torch.uint8, x.device)
+    exps = _buffer(exps, "exps", (B, H, nb), torch.int32, x.device)
+    if signs is not None and (not isinstance(signs, torch.Tensor)
+                              or signs.dtype != torch.float32 or signs.numel() != d
+                              or not signs.is_cuda or signs.device != x.device
+                              or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous float32 tensor of d values on "
+                         "the device of x")
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
         rc = lib().fa2_quantize_fp8(x.data_ptr(), codes.data_ptr(), exps.data_ptr(),
@@ -460,6 +464,8 @@ def forward_fp8(q8, q_exp, k8, k_exp, v8, v_exp, causal: bool = False,
     attention scale of the original inputs (default 1/sqrt(d)).  Returns
     ``(o, lse)``."""
     import torch
+    if not isinstance(q8, torch.Tensor) or q8.dim() != 4:
+        raise ValueError("q8 must be a uint8 tensor [B, H, N, d]")
     B, H, N, d = (int(v) for v in q8.shape)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -467,14 +473,22 @@ def forward_fp8(q8, q_exp, k8, k_exp, v8, v_exp, causal: bool = False,
     fn = {torch.bfloat16: "fa2_fwd_fp8", torch.float32: "fa2_fwd_fp8_o32"}.get(odt)
     if fn is None:
         raise ValueError("out_dtype must be bfloat16 or float32")
+    dev = q8.device
     for t in (q8, k8, v8):
-        if t.dtype != torch.uint8 or tuple(t.shape) != (B, H, N, d) or not t.is_cuda \
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 \
+                or tuple(t.shape) != (B, H, N, d) or not t.is_cuda \
+                or t.device != dev or not t.is_contiguous():
+            raise ValueError("codes must be contiguous uint8 tensors [B, H, N, d] on one GPU")
+    # block exponents: Q per 128-row block, K and V per 64-row block
+    for t, name, rows in ((q_exp, "q_exp", 128), (k_exp, "k_exp", 64), (v_exp, "v_exp", 64)):
+        shape = (B, H, -(-N // rows))
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 \
+                or tuple(t.shape) != shape or not t.is_cuda or t.device != dev \
                 or not t.is_contiguous():
-            raise ValueError("codes must be contiguous uint8 GPU tensors [B, H, N, d]")
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=odt, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+            raise ValueError("%s must be a contiguous int32 tensor %s on the device "
+                             "of the codes" % (name, shape))
+    out = _buffer(out, "out", (B, H, N, d), odt, dev)
+    lse = _buffer(lse, "lse", (B, H, N), torch.float32, dev)
     with torch.cuda.device(q8.device):
         stream = torch.cuda.current_stream(q8.device).cuda_stream
         rc = getattr(lib(), fn)(q8.data_ptr(), q_exp.data_ptr(), k8.data_ptr(),
