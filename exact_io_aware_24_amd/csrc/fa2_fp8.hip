@@ -23,6 +23,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cfloat>
 #include <type_traits>
 
 #include "fa2_device.h"
@@ -311,7 +312,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Params p) {
       vrd[ct] = row * D + (((2 * ct + (g & 1)) ^ vswz<D>(row)) * 16) + 8 * (s & 1);
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // The running reference starts at the lowest finite float instead of
+  // -inf: every finite logit exceeds it by more than the rescale threshold,
+  // so a lane's first visible key raises it, and neither m_run - shift nor
+  // m_run - m_new can form inf - inf (no selects on the tile path).
+  float m_run = -FLT_MAX, l_run = 0.f;
   f32x16 oacc[C::NCT];
 #pragma unroll
   for (int ct = 0; ct < C::NCT; ++ct)
@@ -336,10 +341,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Params p) {
 
   // one tile; MASKED (diagonal or ragged tiles) is a compile-time switch so
   // that the unmasked tiles carry no mask or select instructions
-  // ct_c: this tile's scores -> base-2 logits; shift (<= 0): its V exponent
-  // relative to the head's largest
+  // ct_c: this tile's scores -> base-2 logits; ishift (<= 0): its V
+  // exponent relative to the head's largest
   auto tile = [&](auto masked_tag, int t, const char *kb, const char *vb,
-                  float ct_c, float shift) {
+                  float ct_c, int ishift) {
     constexpr bool masked = decltype(masked_tag)::value;
     f32x16 s[2];
 #pragma unroll
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Params p) {
     const float m_tile = mx == -INFINITY ? -INFINITY : mx * ct_c;
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
       const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[ct][r] *= alpha;
     }
-    const float mu = (m_run == -INFINITY ? 0.f : m_run) - shift;
+    const float mu = m_run - static_cast<float>(ishift);
     float x[2][16];
     float rs = 0.f;
 #pragma unroll
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Params p) {
         x[kt][r] = v;
         rs += v;
       }
-    l_run += ldexpf(rs, -static_cast<int>(shift));  // P = P' 2^-shift
+    l_run += ldexpf(rs, -ishift);  // P = P' 2^-shift
     // P' (<= 2^8) as e4m3, key order 32kt + 8a + 4hh + b -> byte 16kt + 4a + b
     i32x8 pb;
 #pragma unroll
@@ -423,11 +428,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Params p) {
   int ek_n = ntiles > 0 ? kex[0] : 0, ev_n = ntiles > 0 ? vex[0] : 0;
   // the tile constants are formed after the barrier, once the exponents are
   // known to have arrived
-  auto consts = [&](float &ct_c, float &shift) {
+  auto consts = [&](float &ct_c, int &ishift) {
     ct_c = ldexpf(cq, eq + ek_n);
-    shift = static_cast<float>(ev_n - em);
+    ishift = ev_n - em;
   };
-  float ct_c = 0.f, shift = 0.f;
+  float ct_c = 0.f;
+  int shift = 0;
   auto prefetch = [&](int t) {
     if (t + 1 < ntiles) {
       const int nb = (t + 1) & 1;
