@@ -94,6 +94,24 @@ def test_fp8_attention_vs_dequantised(fa2, B, H, N, d, causal):
             assert np.max(np.abs(parity.to_np(lse) - l_ref)) <= 1e-2
 
 
+@pytest.mark.parametrize("N,d", [(200, 128), (77, 64)])
+def test_fp8_zero_scale(fa2, N, d):
+    """scale = 0: every visible key has weight one (the causal mask keeps
+    the prefix), so O is the running mean of the dequantised V rows; the
+    masked scores meet a zero scale on the diagonal tiles."""
+    import torch
+    q, k, v = wl.make_inputs(1, 2, N, d, "bf16", seed=970 + N)
+    for sg in (None, wl.make_signs(d)):
+        say("fp8 attention scale=0 N=%d d=%d causal rotate=%s" % (N, d, sg is not None))
+        o_ref, l_ref, _ = oracle.attention_fp8_reference(
+            q, k, v, 0.0, True, sg.numpy() if sg is not None else None)
+        o, lse = run_fp8(fa2, q, k, v, True, sg, torch.float32, 0.0)
+        res = parity.compare_fp8(parity.to_np(o), o_ref)
+        assert res["finite"] and res["rel_l2"] <= parity.FP8_REL_L2 \
+            and res["max_rel"] <= parity.FP8_MAX_REL, res
+        assert np.max(np.abs(parity.to_np(lse) - l_ref)) <= 1e-2
+
+
 def test_fp8_end_to_end(fa2):
     """Against the exact attention of the original bf16 inputs: within the
     bound on standard normal inputs; with outlier channels the rotation
