@@ -818,15 +818,24 @@ hipError_t launch(const BwdParams &prm, int64_t rows, hipStream_t s) {
                      0, s, prm.o, prm.dout, prm.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (CAUSAL && prm.group > prm.n_gsplits)  // paired blocks, several heads per range
-    hipLaunchKernelGGL((dkdv_pair_kernel<D, O32>), dim3(prm.total_kv), dim3(kThreads), 0, s,
+  unsigned pad = 0;
+  if (CAUSAL && prm.group > prm.n_gsplits) {  // paired blocks, several heads per range
+    e = debug_lds_pad(reinterpret_cast<const void *>(&dkdv_pair_kernel<D, O32>), &pad);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dkdv_pair_kernel<D, O32>), dim3(prm.total_kv), dim3(kThreads), pad, s,
                        prm);
-  else if (prm.group > prm.n_gsplits)  // some range holds several query heads
+  } else if (prm.group > prm.n_gsplits) {  // some range holds several query heads
+    e = debug_lds_pad(reinterpret_cast<const void *>(&dkdv_kernel<D, CAUSAL, O32, true>), &pad);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, O32, true>), dim3(prm.total_kv),
-                       dim3(kThreads), 0, s, prm);
-  else
+                       dim3(kThreads), pad, s, prm);
+  } else {
+    e = debug_lds_pad(reinterpret_cast<const void *>(&dkdv_kernel<D, CAUSAL, O32, false>),
+                      &pad);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, O32, false>), dim3(prm.total_kv),
-                       dim3(kThreads), 0, s, prm);
+                       dim3(kThreads), pad, s, prm);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (prm.n_gsplits > 1) {
@@ -840,8 +849,10 @@ hipError_t launch(const BwdParams &prm, int64_t rows, hipStream_t s) {
       if (e != hipSuccess) return e;
     }
   }
+  e = debug_lds_pad(reinterpret_cast<const void *>(&dq_kernel<D, CAUSAL, O32>), &pad);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dq_kernel<D, CAUSAL, O32>), dim3(prm.total), dim3(kThreads),
-                     0, s, prm);
+                     pad, s, prm);
   return hipGetLastError();
 }
 

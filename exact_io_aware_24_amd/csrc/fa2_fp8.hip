@@ -509,7 +509,11 @@ hipError_t launch_q(const QuantArgs &a, hipStream_t s) {
 
 template <int D, bool CAUSAL, bool O32>
 hipError_t launch_f(const Fp8Params &prm, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, O32>), dim3(prm.total), dim3(kThreads), 0,
+  unsigned pad = 0;
+  const hipError_t e =
+      debug_lds_pad(reinterpret_cast<const void *>(&fwd_fp8_kernel<D, CAUSAL, O32>), &pad);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, O32>), dim3(prm.total), dim3(kThreads), pad,
                      s, prm);
   return hipGetLastError();
 }

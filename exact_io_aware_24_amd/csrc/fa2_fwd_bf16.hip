@@ -1015,12 +1015,20 @@ __global__ __launch_bounds__(kThreads) void merge_splits_kernel(
 // flight); d = 64: fwd_small_kernel (four waves per SIMD, 64-key tiles).
 template <int D, bool CAUSAL, bool O32>
 hipError_t launch(const Params &prm, int grid, hipStream_t s) {
-  if constexpr (D == 64)
+  unsigned pad = 0;
+  if constexpr (D == 64) {
+    const hipError_t e = debug_lds_pad(
+        reinterpret_cast<const void *>(&fwd_small_kernel<D, kSmallTile, CAUSAL, O32>), &pad);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_small_kernel<D, kSmallTile, CAUSAL, O32>), dim3(grid),
-                       dim3(kThreads), 0, s, prm);
-  else
+                       dim3(kThreads), pad, s, prm);
+  } else {
+    const hipError_t e =
+        debug_lds_pad(reinterpret_cast<const void *>(&fwd_bf16_kernel<D, CAUSAL, O32>), &pad);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, O32>), dim3(grid),
-                       dim3(kThreads), 0, s, prm);
+                       dim3(kThreads), pad, s, prm);
+  }
   return hipGetLastError();
 }
 
@@ -1098,6 +1106,18 @@ hipError_t fwd_scratch(float **ptr) {
 static int debug_no_skip() {
   const char *e = std::getenv("FA2_DEBUG_NO_SKIP");
   return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
+hipError_t debug_lds_pad(const void *kernel, unsigned *pad) {
+  *pad = 0;
+  const char *e = std::getenv("FA2_DEBUG_ONE_WG_PER_CU");
+  if (e == nullptr || e[0] != '1' || e[1] != '\0') return hipSuccess;
+  hipFuncAttributes fa;
+  const hipError_t r = hipFuncGetAttributes(&fa, kernel);
+  if (r != hipSuccess) return r;
+  constexpr size_t kTarget = 84u * 1024;  // > 160 KB / 2
+  *pad = fa.sharedSizeBytes < kTarget ? static_cast<unsigned>(kTarget - fa.sharedSizeBytes) : 0;
+  return hipSuccess;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool o32, hipStream_t s) {

@@ -120,8 +120,12 @@ __global__ __launch_bounds__(kThreads) void fwd_fp32_kernel(Params p) {
 
 template <int D, bool CAUSAL>
 hipError_t launch(const Params &prm, int grid, hipStream_t s) {
+  unsigned pad = 0;
+  const hipError_t e =
+      debug_lds_pad(reinterpret_cast<const void *>(&fwd_fp32_kernel<D, CAUSAL>), &pad);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fwd_fp32_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads),
-                     0, s, prm);
+                     pad, s, prm);
   return hipGetLastError();
 }
 

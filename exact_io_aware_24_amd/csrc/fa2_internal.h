@@ -86,6 +86,14 @@ struct Fp8Args {
 };
 hipError_t launch_fwd_fp8(const Fp8Args &a, bool o32, hipStream_t s);
 
+// FA2_DEBUG_ONE_WG_PER_CU=1 in the environment (read at every launch):
+// *pad receives the dynamic LDS to request beside the kernel's static LDS so
+// that one workgroup takes more than half of a compute unit's 160 KB and at
+// most one runs per compute unit.  The kernels never touch that memory; the
+// changed timing and co-residency test their barriers and LDS reuse, which
+// must leave every output bit unchanged.  *pad = 0 when the switch is off.
+hipError_t debug_lds_pad(const void *kernel, unsigned *pad);
+
 // Query rows per workgroup of each kernel (the grid is B*H*ceil(N/rows)).
 constexpr int kBf16RowsPerBlock = 128;
 constexpr int kFp32RowsPerBlock = 64;

@@ -53,6 +53,14 @@
  * enqueued (the only HIP calls before that query the current device and the
  * stream's device), so a rejected call has no effect and enqueues nothing.  A non-zero return is
  * one of the FA2_ERR_* codes below; fa2_strerror() names it.
+ *
+ * Test switch: with FA2_DEBUG_ONE_WG_PER_CU=1 in the environment at the time
+ * of a call, the attention kernels of every entry point (forward, fp32,
+ * FP8, backward) are launched with dynamic LDS that they never touch, enough
+ * that a workgroup takes more than half of a compute unit's 160 KB and at
+ * most one runs per compute unit.  The outputs must keep the same bits: a
+ * missing barrier or an LDS buffer reused too early would show under the
+ * changed timing.  It costs time.
  */
 #ifndef FA2_H
 #define FA2_H
