@@ -168,8 +168,8 @@ int fa2_fwd_gqa_o32(const void *q, const void *k, const void *v, float *o,
  *              (may be NULL) and the call is one kernel launch
  *   o_part   : float [n_splits][B][H][Nq][d] caller-owned workspace
  *   lse_part : float [n_splits][B][H][Nq] caller-owned workspace
- * Range s covers key tiles [s*T, (s+1)*T) with T = ceil(ceil(Nk/BC) /
- * n_splits) (BC = 64 keys at d = 128, 128 at d = 64); ranges past the end
+ * Range s covers key tiles [s*T, (s+1)*T) with T = ceil(ceil(Nk/64) /
+ * n_splits) (tiles of 64 keys at d = 64 and d = 128); ranges past the end
  * are empty and contribute nothing.  The workspaces must not overlap any
  * input, output or each other (FA2_ERR_ALIAS); n_splits outside its range or
  * a grid over 2^31 - 1 workgroups is FA2_ERR_SHAPE.  Results depend on
