@@ -117,9 +117,12 @@ struct Params {
   float c;               // scale * log2(e)
 };
 
+// Tile configuration of fwd_bf16_kernel, which runs d = 128 only (d = 64
+// runs fwd_small_kernel with its own SmallCfg).
 template <int D>
 struct Cfg {
-  static constexpr int BC = (D == 128) ? 64 : 128;  // keys per tile
+  static_assert(D == 128, "fwd_bf16_kernel is the d = 128 kernel");
+  static constexpr int BC = 64;                     // keys per tile
   static constexpr int KCH = D / 8;                 // 16-byte granules per K row
   static constexpr int NKT = BC / 32;               // 32-key sub-tiles
   static constexpr int NDT = D / 16;                // 16-dim MFMA k-steps
@@ -180,12 +183,9 @@ __device__ __forceinline__ void issue_v(const uint16_t *v, int head_bytes,
   const u32x4 rv = tile_desc(v, head_bytes, tile_byte);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    // d = 128: block of 32 columns = wave, 16-key group = it;
-    // d = 64: block = wave / 2, 16-key group = 4 * (wave & 1) + it
-    const int cg = (D == 128) ? wv : (wv >> 1);
-    const int kb = (D == 128) ? it : (4 * (wv & 1) + it);
+    // block of 32 columns = wave, 16-key group = it
     const int vo = off.v_ld[it];
-    dma16(rv, vo, 0, lds_addr(vbuf + cg * C::BC * 64 + kb * 1024));
+    dma16(rv, vo, 0, lds_addr(vbuf + wv * C::BC * 64 + it * 1024));
   }
 }
 
@@ -378,11 +378,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     off.k_ld[it] = row * D * 2 + ((pos ^ kswz<D>(row)) * 16);
   }
   {
-    const int cg = (D == 128) ? wv : (wv >> 1);
-    const int kb0 = (D == 128) ? 0 : 4 * (wv & 1);
 #pragma unroll
     for (int it = 0; it < 4; ++it)
-      off.v_ld[it] = (16 * (kb0 + it) + lane / 4) * D * 2 + (4 * cg + (lane & 3)) * 16;
+      off.v_ld[it] = (16 * it + lane / 4) * D * 2 + (4 * wv + (lane & 3)) * 16;
   }
 
   float c = p.c;
@@ -410,9 +408,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int xcd = static_cast<int>(blockIdx.x & 7);
   const int ilo = static_cast<int>(static_cast<int64_t>(xcd) * p.total / 8);
   const int ilen = static_cast<int>(static_cast<int64_t>(xcd + 1) * p.total / 8) - ilo;
-  constexpr bool kCanPersist = D == 128;  // (d = 64 runs fwd_small_kernel)
   auto item_at = [&](int r) -> int {
-    if (!kCanPersist || !p.persist) return r == 0 ? xcd_remap(blockIdx.x, p.total) : -1;
+    if (!p.persist) return r == 0 ? xcd_remap(blockIdx.x, p.total) : -1;
     const int local = r * per + ((r & 1) ? per - 1 - xj : xj);
     return local < ilen ? ilo + local : -1;
   };
