@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(Fp8Params p) {
     float mlo, mhi;
     halves(mx, mlo, mhi);
     mx = fmaxf(mlo, mhi);
-    const float m_tile = mx == -INFINITY ? -INFINITY : mx * ct_c;
+    const float m_tile = (masked && mx == -INFINITY) ? -INFINITY : mx * ct_c;
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = fast_exp2(m_run - m_new);
