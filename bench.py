@@ -304,7 +304,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only (this build runs no multi-GPU "
+        print("bench.py measures one GPU only (the library has no multi-GPU "
               "path); got --gpus %d" % args.gpus, file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
