@@ -529,3 +529,49 @@ def raw_call_bwd_gqa(fn: str, ptrs, B, H, H_kv, N, d, scale, causal, n_gsplits,
         raise ValueError("ten pointers expected")
     return int(getattr(lib(), fn)(*ptrs, B, H, H_kv, N, d, ctypes.c_float(scale),
                                   int(causal), n_gsplits, dkv_part, stream))
+
+
+_ATTENTION_FN = None
+
+
+def _attention_fn():
+    """The autograd Function behind :func:`attention` (built on first use so
+    that importing the package does not import torch)."""
+    global _ATTENTION_FN
+    if _ATTENTION_FN is None:
+        import torch
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, causal, scale):
+                o, lse = forward(q, k, v, causal=causal, scale=scale)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.causal, ctx.scale = causal, scale
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                dq, dk, dv = backward(q, k, v, o, do.contiguous(), lse,
+                                      causal=ctx.causal, scale=ctx.scale)
+                return dq, dk, dv, None, None
+
+        _ATTENTION_FN = _Attention
+    return _ATTENTION_FN
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None):
+    """Exact attention as a differentiable torch operation: the output of
+    :func:`forward` (bfloat16 ``[B, H, N, d]``), whose gradient with respect
+    to ``q, k, v`` :func:`backward` computes from the saved output and
+    log-sum-exp.  ``q``: ``[B, H, N, d]``, ``k, v``: ``[B, H, N, d]`` or
+    ``[B, H_kv, N, d]`` with H_kv dividing H; all contiguous bfloat16 GPU
+    tensors (the backward pass exists for bfloat16 only).  Both passes are
+    enqueued on torch's current stream."""
+    import torch
+    _check_tensors(q, k, v, grouped=True)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("attention() needs bfloat16 q, k, v (the backward pass is bf16)")
+    d = int(q.shape[-1])
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    return _attention_fn().apply(q, k, v, bool(causal), s)
