@@ -378,7 +378,8 @@ def main(argv=None):
     elif decode:
         flops = w.flops
         entry = "fa2_fwd_splitkv"
-        n_splits = args.splits or fa2.default_splits(w.B, w.H, w.q_rows, w.N, w.d)
+        n_splits = args.splits or fa2.default_splits(w.B, w.H, w.q_rows, w.N, w.d,
+                                                     w.kv_heads, w.causal)
         o = torch.empty(qd.shape, dtype=out_dtype, device=dev)
         o_part = torch.empty((n_splits,) + tuple(qd.shape), dtype=torch.float32, device=dev)
         lse_part = torch.empty((n_splits,) + tuple(qd.shape[:3]), dtype=torch.float32,

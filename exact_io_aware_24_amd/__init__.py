@@ -318,15 +318,27 @@ def backward(q, k, v, o, dout, lse, causal: bool = False,
     return dq, dk, dv
 
 
-def default_splits(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
-    """A key-range count that gives the GPU about 1024 workgroups (two per
-    compute unit, twice over) while keeping every range at least four key
-    tiles long."""
-    blocks = B * H * ((Nq + 127) // 128)
-    tile = 64  # keys per tile of the bf16 kernels, d = 64 and d = 128 alike
-    tiles = (Nk + tile - 1) // tile
-    n = -(-1024 // blocks)
-    return int(max(1, min(n, tiles // 4, MAX_SPLITS)))
+def default_splits(B: int, H: int, Nq: int, Nk: int, d: int, H_kv: int | None = None,
+                   causal: bool = False) -> int:
+    """A key-range count for :func:`forward_splitkv`.  With K/V heads shared
+    by H / H_kv query heads, fewer than 128 queries per head and every query
+    seeing the same keys (no mask, or one query), the library runs a group's
+    rows in one workgroup, and the block count follows that.  Blocks with
+    fewer than 128 rows (decoding) are bound by streaming K and V: about 512
+    workgroups in all (two per compute unit) with ranges of at least 32 key
+    tiles measured best on decode shapes; full blocks are bound by the
+    matrix cores and get about 1024 workgroups with ranges of at least four
+    tiles."""
+    hk = H if H_kv is None else H_kv
+    packed = hk < H and Nq < 128 and (Nq == 1 or not causal)
+    rows = Nq * (H // hk) if packed else Nq
+    blocks = B * (hk if packed else H) * ((rows + 127) // 128)
+    tiles = (Nk + 63) // 64  # keys per tile of the bf16 kernels: 64 at both d
+    if rows < 128:
+        n, cap = -(-512 // blocks), tiles // 32
+    else:
+        n, cap = -(-1024 // blocks), tiles // 4
+    return int(max(1, min(n, cap, MAX_SPLITS)))
 
 
 def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
@@ -352,7 +364,7 @@ def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if n_splits is None:
-        n_splits = default_splits(B, H, Nq, Nk, d)
+        n_splits = default_splits(B, H, Nq, Nk, d, H_kv, causal)
     odt = torch.bfloat16 if out_dtype is None else out_dtype
     fn = {torch.bfloat16: "fa2_fwd_splitkv", torch.float32: "fa2_fwd_splitkv_o32"}.get(odt)
     if fn is None:
@@ -397,7 +409,7 @@ def forward_splitkv_noalloc(q, k, v, causal: bool = False,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if n_splits is None:
-        n_splits = default_splits(B, H, Nq, Nk, d)
+        n_splits = default_splits(B, H, Nq, Nk, d, H_kv, causal)
     dev = q.device
     out = _buffer(out, "out", (B, H, Nq, d), torch.bfloat16, dev)
     lse = _buffer(lse, "lse", (B, H, Nq), torch.float32, dev) if return_lse else None

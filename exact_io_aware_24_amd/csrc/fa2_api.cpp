@@ -95,6 +95,23 @@ fa2::FwdArgs make_args(const void *q, const void *k, const void *v, void *o,
   return a;
 }
 
+// Few queries per head and shared K/V heads (decoding with grouped-query
+// attention): the query heads of one K/V head are consecutive in q, o and
+// lse, so their rows form one [group * Nq, d] matrix against that K/V head.
+// Launched that way, one workgroup takes the rows of a whole group and
+// streams the K/V head once per key range instead of once per query head.
+// Each row's result is the same computation (rows only move between lanes
+// and waves).  Used where every packed row sees the same keys: without a
+// mask, or with one query per head, which sees every key when causal.
+void pack_query_heads(fa2::FwdArgs &a) {
+  if (a.group == 1 || a.nq >= fa2::kBf16RowsPerBlock || (a.causal && a.nq != 1)) return;
+  a.bh /= a.group;
+  a.h /= a.group;
+  a.nq *= a.group;
+  a.group = 1;
+  a.causal = false;  // one query per head sees every key
+}
+
 // Validation of the backward entry points: every pointer is required (the
 // partial-sum workspace only when n_gsplits > 1); the outputs (dq, dk, dv,
 // the delta workspace and the partial-sum workspace) may overlap neither an
@@ -200,9 +217,9 @@ FA2_EXPORT int fa2_fwd_gqa(const void *q, const void *k, const void *v,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc == FA2_OK) rc = check_stream(stream);
   if (rc != FA2_OK) return rc;
-  return finish(fa2::launch_fwd_bf16(
-      make_args(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, causal), false,
-      static_cast<hipStream_t>(stream)));
+  fa2::FwdArgs a = make_args(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, causal);
+  pack_query_heads(a);
+  return finish(fa2::launch_fwd_bf16(a, false, static_cast<hipStream_t>(stream)));
 }
 
 FA2_EXPORT int fa2_fwd_gqa_o32(const void *q, const void *k, const void *v,
@@ -213,9 +230,9 @@ FA2_EXPORT int fa2_fwd_gqa_o32(const void *q, const void *k, const void *v,
                     fa2::kBf16RowsPerBlock, FA2_MAX_HEAD_ELEMS_BF16);
   if (rc == FA2_OK) rc = check_stream(stream);
   if (rc != FA2_OK) return rc;
-  return finish(fa2::launch_fwd_bf16(
-      make_args(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, causal), true,
-      static_cast<hipStream_t>(stream)));
+  fa2::FwdArgs a = make_args(q, k, v, o, lse, B, H, H_kv, N, N, d, scale, causal);
+  pack_query_heads(a);
+  return finish(fa2::launch_fwd_bf16(a, true, static_cast<hipStream_t>(stream)));
 }
 
 FA2_EXPORT int fa2_fwd_o32(const void *q, const void *k, const void *v,
@@ -266,6 +283,7 @@ static int splitkv(const void *q, const void *k, const void *v, void *o, float *
   a.n_splits = n_splits;
   a.o_part = o_part;
   a.lse_part = lse_part;
+  pack_query_heads(a);
   return finish(fa2::launch_fwd_bf16(a, o32, static_cast<hipStream_t>(stream)));
 }
 
@@ -316,6 +334,7 @@ FA2_EXPORT int fa2_fwd_splitkv_noalloc(const void *q, const void *k,
   if (rc != FA2_OK) return rc;
   fa2::FwdArgs a = make_args(q, k, v, o, lse, B, H, H_kv, Nq, Nk, d, scale, causal);
   a.n_splits = n_splits;
+  pack_query_heads(a);
   if (n_splits > 1) {
     float *ws = nullptr;
     if (fa2::fwd_scratch(&ws) != hipSuccess) return FA2_ERR_HIP;

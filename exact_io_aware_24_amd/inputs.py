@@ -89,6 +89,9 @@ WORKLOADS = {
         # decoding one token against a 16384-entry key/value cache
         Workload("decode_b8h32_nq1_nk16384_d128", 8, 32, 16384, 128, False,
                  "bf16", Nq=1),
+        # the same with 4 query heads per K/V head (grouped-query decoding)
+        Workload("decode_gqa_b8h32kv8_nq1_nk16384_d128", 8, 32, 16384, 128, False,
+                 "bf16", H_kv=8, Nq=1),
     ]
 }
 HEADLINE = "causal_b2h16_n8192_d128"

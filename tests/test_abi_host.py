@@ -327,11 +327,19 @@ def test_splitkv_noalloc_validation(L):
 
 
 def test_default_splits():
-    # decode: one query block per head -> split up to ~1024 workgroups
-    assert fa2.default_splits(8, 32, 1, 16384, 128) == 4
-    assert fa2.default_splits(1, 1, 1, 65536, 128) == 256
-    # short keys: never below four tiles per range
+    # decode (blocks of fewer than 128 rows): about 512 workgroups, ranges of
+    # at least 32 key tiles
+    assert fa2.default_splits(8, 32, 1, 16384, 128) == 2
+    assert fa2.default_splits(1, 1, 1, 65536, 128) == 32
+    # grouped decode: a group's query heads share one block
+    assert fa2.default_splits(8, 32, 1, 16384, 128, 8, True) == 8
+    assert fa2.default_splits(1, 32, 1, 65536, 128, 8, True) == 32
+    # a causal mask over several queries keeps the heads apart
+    assert fa2.default_splits(8, 32, 4, 16384, 128, 8, True) == 2
+    # short keys: never a range below the minimum length
     assert fa2.default_splits(1, 1, 1, 300, 128) == 1
+    # full blocks: about 1024 workgroups, ranges of at least four tiles
+    assert fa2.default_splits(1, 2, 130, 4096, 128) == 16
     # already enough workgroups: no split
     assert fa2.default_splits(2, 16, 8192, 8192, 128) == 1
 

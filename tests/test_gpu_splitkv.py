@@ -60,6 +60,12 @@ CASES = [
     (1, 1, 1, 2, 100, 128, False, 16),     # more ranges than key tiles
     (1, 2, 2, 300, 100, 128, True, 2),     # more queries than keys
     (2, 2, 2, 256, 256, 128, True, 3),     # square, split
+    # shared K/V heads with few queries: a group's rows run as one matrix
+    (2, 8, 2, 1, 1000, 128, True, 3),      # grouped decode (one query sees all keys)
+    (1, 8, 1, 1, 700, 64, False, 1),       # multi-query decode, one range, d = 64
+    (2, 8, 2, 5, 900, 128, False, 2),      # a few queries per head, no mask
+    (1, 16, 2, 100, 600, 128, False, 1),   # 800 rows per group: blocks span heads
+    (1, 32, 4, 1, 4096, 128, True, 16),    # eight query heads per K/V head
 ]
 
 
@@ -88,6 +94,23 @@ def test_splitkv_vs_oracle(fa2, B, H, Hk, Nq, Nk, d, causal, S):
         assert res["ok"], parity.describe(res)
 
 
+@pytest.mark.parametrize("N,causal", [(1, True), (40, False), (130, False)])
+def test_grouped_short_sequences(fa2, N, causal):
+    """fa2_fwd_gqa with fewer than 128 rows per head and every row seeing
+    the same keys runs each group's rows together; against the oracle."""
+    import torch
+    q, k, v = wl.make_inputs(2, 8, N, 128, "bf16", seed=760 + N, H_kv=2)
+    scale = 1.0 / math.sqrt(128)
+    o_ref, l_ref, _ = reference(q, k, v, scale, causal)
+    dev = torch.device("cuda:0")
+    say("grouped forward N=%d causal=%s" % (N, causal))
+    o, lse = fa2.forward(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale,
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    res = parity.compare(parity.to_np(o), o_ref, parity.to_np(lse), l_ref, "fp32")
+    assert res["ok"], parity.describe(res)
+
+
 def test_one_range_equals_fa2_fwd(fa2):
     """With equal lengths and one key range the general entry point runs the
     same kernel as fa2_fwd: bit-identical outputs."""
@@ -101,11 +124,14 @@ def test_one_range_equals_fa2_fwd(fa2):
     assert torch.equal(a[0], o.cpu()) and torch.equal(a[1], lse.cpu())
 
 
-def test_decode_workload_full_size(fa2):
-    """The decode workload at full size with the default range count: every
-    row against the oracle (one query row per head)."""
+@pytest.mark.parametrize("name", ["decode_b8h32_nq1_nk16384_d128",
+                                  "decode_gqa_b8h32kv8_nq1_nk16384_d128"])
+def test_decode_workload_full_size(fa2, name):
+    """The decode workloads at full size with the default range count: every
+    row against the oracle (one query row per head; with grouped K/V heads a
+    group's rows run together)."""
     import torch
-    w = wl.WORKLOADS["decode_b8h32_nq1_nk16384_d128"]
+    w = wl.WORKLOADS[name]
     q, k, v = wl.workload_inputs(w)
     say("decode workload %s" % w.describe())
     dev = torch.device("cuda:0")
