@@ -138,6 +138,13 @@ int fa2_fwd_o32(const void *q, const void *k, const void *v, float *o,
  *   H_kv : >= 1 and dividing H (else FA2_ERR_SHAPE); query head h of batch
  *          index b uses key/value head h / (H / H_kv) of the same b
  * Every other argument, the lse output and the error rules are fa2_fwd's.
+ * With N < 128 and a mask that does not vary by row (non-causal, or
+ * N == 1), the H / H_kv query heads of one key/value head are computed as
+ * one block of (H / H_kv) * N rows, so each key/value tile is read once per
+ * key/value head.  Rows then share a wavefront with rows of other heads;
+ * the wavefront's common rescale points change the fp32/bf16 rounding (not
+ * the stated accuracy), so such a call need not match fa2_fwd on repeated
+ * key/value heads bit for bit.  Larger or causal blocks do match it.
  */
 int fa2_fwd_gqa(const void *q, const void *k, const void *v, void *o,
                 float *lse, int B, int H, int H_kv, int N, int d, float scale,
@@ -173,7 +180,12 @@ int fa2_fwd_gqa_o32(const void *q, const void *k, const void *v, float *o,
  * are empty and contribute nothing.  The workspaces must not overlap any
  * input, output or each other (FA2_ERR_ALIAS); n_splits outside its range or
  * a grid over 2^31 - 1 workgroups is FA2_ERR_SHAPE.  Results depend on
- * n_splits only through fp32 rounding in the merge.
+ * n_splits only through rounding (each range keeps its own running maximum,
+ * and the merge is fp32).  With Nq < 128 and H_kv < H, the query heads of
+ * one key/value head are packed into one block exactly as fa2_fwd_gqa
+ * describes (non-causal, or Nq == 1); the workspace layout is unchanged,
+ * since [B][H][Nq] with h = h_kv * (H / H_kv) + g is the same memory as
+ * [B][H_kv][(H / H_kv) * Nq].
  */
 int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o,
                     float *lse, int B, int H, int H_kv, int Nq, int Nk, int d,
