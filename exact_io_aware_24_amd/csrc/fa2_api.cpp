@@ -102,9 +102,13 @@ fa2::FwdArgs make_args(const void *q, const void *k, const void *v, void *o,
 // streams the K/V head once per key range instead of once per query head.
 // Each row's result is the same computation (rows only move between lanes
 // and waves).  Used where every packed row sees the same keys: without a
-// mask, or with one query per head, which sees every key when causal.
+// mask, or with one query per head, which sees every key when causal.  The
+// packed head must still fit the kernel's 32-bit per-head byte offsets (the
+// bound validate() applies to one head): with tens of thousands of query
+// heads per K/V head it would not, and such calls run unpacked.
 void pack_query_heads(fa2::FwdArgs &a) {
   if (a.group == 1 || a.nq >= fa2::kBf16RowsPerBlock || (a.causal && a.nq != 1)) return;
+  if (static_cast<int64_t>(a.group) * a.nq * a.d > FA2_MAX_HEAD_ELEMS_BF16) return;
   a.bh /= a.group;
   a.h /= a.group;
   a.nq *= a.group;

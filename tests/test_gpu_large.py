@@ -111,3 +111,47 @@ def test_decode_at_the_key_limit(fa2):
         res = parity.compare(parity.to_np(o[0, h].cpu()), o_ref,
                              parity.to_np(lse[0, h].cpu()), l_ref, "fp32")
         assert res["ok"], "head %d: %s" % (h, parity.describe(res))
+
+
+@pytest.mark.parametrize("entry", ["forward", "splitkv"])
+def test_grouped_heads_at_the_packing_limit(fa2, entry):
+    """One K/V head shared by tens of thousands of query heads of 127 rows.
+    Short grouped query blocks run as one block of (H / H_kv) * Nq rows per
+    K/V head while that packed head fits the per-head offset range (N*d <=
+    2^30 - 2^16): 66048 query heads pack to exactly 2^30 - 2^16 elements,
+    66052 heads would exceed it and run unpacked.  Sampled heads of both are
+    compared with the oracle."""
+    import torch
+    d, nq = 128, 127
+    nk = nq if entry == "forward" else 300
+    h_big = 66052
+    g = torch.Generator(device="cpu").manual_seed(4545)
+    q = torch.empty(1, h_big, nq, d, dtype=torch.bfloat16)
+    step = 4096
+    for a in range(0, h_big, step):  # drawn in chunks to bound the fp32 temporaries
+        b = min(h_big, a + step)
+        q[0, a:b] = torch.randn(b - a, nq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 1, nk, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(1, 1, nk, d, generator=g).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda:0")
+    qd_all, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    rows = np.arange(nq, dtype=np.int64)
+    for H in (66048, h_big):
+        qd = qd_all[:, :H]
+        say("%s grouped heads B=1 H=%d H_kv=1 Nq=%d Nk=%d d=%d (packed rows %d)"
+            % (entry, H, nq, nk, d, H * nq))
+        if entry == "forward":
+            o, lse = fa2.forward(qd, kd, vd, causal=False, scale=scale, out_dtype=torch.float32)
+        else:
+            o, lse = fa2.forward_splitkv(qd, kd, vd, causal=False, scale=scale, n_splits=2,
+                                         out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(lse).all())
+        for h in (0, 1, H // 2, H - 2, H - 1):
+            o_ref, l_ref, _ = oracle.attention_rows(q[0, h], rows, k[0, 0], v[0, 0], scale, False)
+            res = parity.compare(parity.to_np(o[0, h].cpu()), o_ref,
+                                 parity.to_np(lse[0, h].cpu()), l_ref, "fp32")
+            assert res["ok"], "H=%d head %d: %s" % (H, h, parity.describe(res))
+        del o, lse
+        torch.cuda.empty_cache()
