@@ -293,6 +293,8 @@ def backward(q, k, v, o, dout, lse, causal: bool = False,
     dq, dk, dv = grad(dq, "dq", q), grad(dk, "dk", k), grad(dv, "dv", v)
     if grouped:
         ns = default_gsplits(B, H, Hk, N) if n_gsplits is None else int(n_gsplits)
+        if not 1 <= ns <= H // Hk:  # before the workspace is sized from it
+            raise ValueError("n_gsplits must be in 1..H / H_kv = %d" % (H // Hk))
         if ns > 1 and dkv_part is None:
             dkv_part = torch.empty((2, ns, B, Hk, N, d), dtype=torch.float32,
                                    device=q.device)
@@ -365,6 +367,8 @@ def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
         scale = 1.0 / math.sqrt(d)
     if n_splits is None:
         n_splits = default_splits(B, H, Nq, Nk, d, H_kv, causal)
+    if not 1 <= int(n_splits) <= MAX_SPLITS:  # before any workspace is sized from it
+        raise ValueError("n_splits must be in 1..%d" % MAX_SPLITS)
     odt = torch.bfloat16 if out_dtype is None else out_dtype
     fn = {torch.bfloat16: "fa2_fwd_splitkv", torch.float32: "fa2_fwd_splitkv_o32"}.get(odt)
     if fn is None:
@@ -410,6 +414,8 @@ def forward_splitkv_noalloc(q, k, v, causal: bool = False,
         scale = 1.0 / math.sqrt(d)
     if n_splits is None:
         n_splits = default_splits(B, H, Nq, Nk, d, H_kv, causal)
+    if not 1 <= int(n_splits) <= MAX_SPLITS:
+        raise ValueError("n_splits must be in 1..%d" % MAX_SPLITS)
     dev = q.device
     out = _buffer(out, "out", (B, H, Nq, d), torch.bfloat16, dev)
     lse = _buffer(lse, "lse", (B, H, Nq), torch.float32, dev) if return_lse else None

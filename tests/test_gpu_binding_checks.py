@@ -3,9 +3,10 @@ outputs and workspaces (out, lse, o_part, lse_part, codes, exps, the FP8
 block exponents, the sign vector) must have the shape, dtype, layout and
 device the kernels write or read; the C ABI takes bare pointers and cannot
 see their sizes, so the binding rejects a wrong buffer with ValueError
-before anything is enqueued.  The rejected calls launch nothing; the last
-test runs one valid call with oversized workspaces and compares it with
-the call that allocates its own.  Every case prints its name first."""
+before anything is enqueued, and out-of-range key-range or query-head-range
+counts before a workspace is sized from them.  The rejected calls launch
+nothing; one test runs a valid call with oversized workspaces and compares
+it with the call that allocates its own.  Every case prints its name first."""
 import sys
 
 import pytest
@@ -61,6 +62,11 @@ def test_splitkv_buffers(env):
             o_part=torch.empty(2, B, H, N, d, dtype=torch.bfloat16, device=dev))
     rejects(m.forward_splitkv, q, k, v, n_splits=2,
             out=torch.empty(B, H, N, d + 1, dtype=torch.bfloat16, device=dev))
+    say("forward_splitkv[_noalloc]: key-range counts out of range, rejected before any "
+        "workspace is sized from them")
+    for ns in (0, -1, m.MAX_SPLITS + 1, 1 << 40):
+        rejects(m.forward_splitkv, q, k, v, n_splits=ns)
+        rejects(m.forward_splitkv_noalloc, q, k, v, n_splits=ns)
     say("forward_splitkv_noalloc: wrong out / lse buffers")
     rejects(m.forward_splitkv_noalloc, q, k, v, n_splits=2,
             out=torch.empty(B, H, N, d, **f32))
@@ -105,3 +111,14 @@ def test_oversized_workspaces_work(env):
     o2, l2 = m.forward_splitkv(q, k, v, causal=True, n_splits=2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_backward_range_count(env):
+    m, torch, dev, q, k, v = env
+    B, H, N, d = q.shape
+    kv = k[:, :1].contiguous(), v[:, :1].contiguous()
+    o, lse = m.forward(q, *kv)
+    say("backward: query-head range counts outside 1..H/H_kv rejected before the "
+        "workspace is sized from them")
+    for ns in (0, -3, H + 1, 1 << 40):
+        rejects(m.backward, q, *kv, o, o, lse, n_gsplits=ns)
