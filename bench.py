@@ -490,6 +490,22 @@ def main(argv=None):
         roofline = {"bound": "mfma", "achieved": round(tflops, 3),
                     "peak": peak, "unit": "TFLOP/s",
                     "frac": round(tflops / peak, 4), "traffic": traffic}
+    # what one timed call launches, i.e. what the HIP-event duration behind
+    # roofline.achieved covers
+    if decode:
+        roofline_scope = ("the call launches the key-range kernel and, with n_splits > 1, "
+                          "the merge kernel; achieved = compulsory bytes per call / the "
+                          "call's mean duration, both kernels included (the range kernel "
+                          "alone is in the rocprofv3 trace summary)")
+    elif args.which == "bwd":
+        roofline_scope = ("the call launches the delta, dK/dV and dQ kernels (and, for "
+                          "grouped K/V heads with several ranges, the partial-sum "
+                          "reductions); achieved = the five products' flop per call / the "
+                          "call's mean duration (per-kernel figures are in the rocprofv3 "
+                          "trace summary)")
+    else:
+        roofline_scope = ("the call is one kernel launch; achieved = its flop per launch / "
+                          "its mean duration")
     rec = {
         "metric": "attention %s TFLOP/s (1 MI355X) and %% of bf16 MFMA peak" % args.which,
         "value": round(tflops, 3),
@@ -508,6 +524,7 @@ def main(argv=None):
                    "scale": w.scale, "flops_per_step": flops, "entry_point": entry,
                    "n_splits": n_splits, "n_gsplits": n_gsplits},
         "roofline": roofline,
+        "roofline_scope": roofline_scope,
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "score_matrix_bytes_not_written": score_matrix_bytes(w.B, w.H, w.N),
         "compulsory_hbm_bytes": comp,
