@@ -16,6 +16,6 @@ typedef struct ihipStream_t *hipStream_t;
 typedef int hipDevice_t;
 #define hipStreamLegacy ((hipStream_t)1)
 #define hipStreamPerThread ((hipStream_t)2)
-/* defined by the driver, which decides what they report */
+/* defined by the sanitizer test program, which decides what they report */
 hipError_t hipGetDevice(int *device);
 hipError_t hipStreamGetDevice(hipStream_t stream, hipDevice_t *device);
