@@ -31,8 +31,10 @@ hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t *device) {
 }
 
 namespace fa2 {
+FwdArgs g_last_fwd;  // what the last bf16 forward launch was given
 hipError_t launch_fwd_bf16(const FwdArgs &a, bool, hipStream_t) {
   ++g_launches;
+  g_last_fwd = a;
   if (a.n_splits > 1 && (!a.o_part || !a.lse_part)) return hipErrorInvalidValue;
   return g_result;
 }
@@ -58,6 +60,8 @@ static int g_fail = 0;
 
 // fake, never dereferenced device addresses, 64 MiB apart
 static void *P(int i) { return reinterpret_cast<void *>(uintptr_t(0x10000000) + uintptr_t(i) * (64u << 20)); }
+// the same, 16 GiB apart (calls whose tensors exceed 64 MiB)
+static void *FAR(int i) { return reinterpret_cast<void *>((uintptr_t(1) << 40) + uintptr_t(i) * (uintptr_t(1) << 34)); }
 static float *F(int i) { return static_cast<float *>(P(i)); }
 static void *off(void *p, int bytes) { return static_cast<char *>(p) + bytes; }
 
@@ -98,6 +102,46 @@ int main() {
   EXPECT(fa2_fwd_gqa(P(0), P(1), P(2), P(3), F(4), 2, 8, 2, 300, 128, 0.1f, 1, nullptr), FA2_OK);
   EXPECT(fa2_fwd_gqa(P(0), P(1), P(2), P(3), F(4), 2, 8, 3, 300, 128, 0.1f, 1, nullptr), FA2_ERR_SHAPE);
   EXPECT(fa2_fwd_gqa(P(0), P(1), P(2), P(3), F(4), 2, 8, 0, 300, 128, 0.1f, 1, nullptr), FA2_ERR_SHAPE);
+  // grouped short query blocks: the query heads of one K/V head are launched
+  // as one block of (H / H_kv) * Nq unmasked rows when every row sees the
+  // same keys and the packed head fits the per-head bound
+  struct Pack { int B, H, Hkv, Nq, Nk, d, causal; bool packed; };
+  const Pack packs[] = {
+      {8, 32, 8, 1, 16384, 128, 1, true},      // decoding: one query sees every key
+      {8, 32, 8, 1, 16384, 128, 0, true},
+      {2, 8, 2, 40, 300, 64, 0, true},         // short blocks, no mask
+      {2, 8, 2, 4, 300, 128, 1, false},        // causal with several queries: per-row mask
+      {2, 8, 2, 128, 300, 128, 0, false},      // full blocks
+      {2, 8, 8, 1, 300, 128, 0, false},        // no shared K/V heads
+      {1, 66048, 1, 127, 300, 128, 0, true},   // packed head exactly at the per-head bound
+      {1, 66052, 1, 127, 300, 128, 0, false},  // one that would pass it
+  };
+  for (const Pack &c : packs) {
+    EXPECT(fa2_fwd_splitkv(FAR(0), FAR(1), FAR(2), FAR(3), static_cast<float *>(FAR(4)), c.B, c.H,
+                           c.Hkv, c.Nq, c.Nk, c.d, 0.1f, c.causal, 1, nullptr, nullptr, nullptr),
+           FA2_OK);
+    const fa2::FwdArgs &a = fa2::g_last_fwd;
+    const int g = c.H / c.Hkv;
+    const bool ok = c.packed ? (a.bh == c.B * c.Hkv && a.h == c.Hkv && a.group == 1 &&
+                                a.nq == c.Nq * g && a.nk == c.Nk && !a.causal)
+                             : (a.bh == c.B * c.H && a.h == c.H && a.group == g &&
+                                a.nq == c.Nq && a.nk == c.Nk && a.causal == (c.causal != 0));
+    if (!ok) {
+      std::printf("FAIL packing B=%d H=%d H_kv=%d Nq=%d causal=%d: bh=%d h=%d group=%d nq=%d "
+                  "causal=%d\n", c.B, c.H, c.Hkv, c.Nq, c.causal, a.bh, a.h, a.group, a.nq,
+                  int(a.causal));
+      ++g_fail;
+    }
+  }
+  // the grouped forward packs the same way (N < 128, no mask)
+  EXPECT(fa2_fwd_gqa(P(0), P(1), P(2), P(3), F(4), 2, 8, 2, 100, 128, 0.1f, 0, nullptr), FA2_OK);
+  const fa2::FwdArgs &gq = fa2::g_last_fwd;
+  if (!(gq.bh == 4 && gq.nq == 400 && gq.nk == 100 &&
+        gq.group == 1)) {
+    std::printf("FAIL fa2_fwd_gqa packing: bh=%d nq=%d nk=%d group=%d\n", gq.bh,
+                gq.nq, gq.nk, gq.group);
+    ++g_fail;
+  }
   // split key ranges, caller workspaces
   EXPECT(fa2_fwd_splitkv(P(0), P(1), P(2), P(3), F(4), 1, 4, 2, 16, 1000, 128, 0.1f, 1, 4, F(5),
                          F(6), nullptr), FA2_OK);

@@ -6,7 +6,9 @@
   (tests/sanitize/), and driven through valid and invalid calls of every
   entry point: each valid call must reach exactly one launcher, each invalid
   one must return its code without launching, and the sanitizers must stay
-  silent.
+  silent.  The bf16 forward launcher records its arguments, so the host's
+  packing of grouped short query blocks (which calls run the query heads of
+  a K/V head as one block, and which stay unpacked) is checked as well.
 * The fp64 oracle (oracle/attn_oracle.c) is built with gcc and both
   sanitizers and every oracle pin runs against that build in a child
   process with the AddressSanitizer runtime preloaded.
