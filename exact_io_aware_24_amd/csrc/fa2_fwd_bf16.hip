@@ -34,7 +34,13 @@
 // leaves the rounding of a dominant P~ -- anywhere in (1, 2^8] under the lazy
 // rescale, not exactly 1 -- in O undiluted, up to 2^-8 of |V|, which exceeds
 // the stated tolerance on sharp softmaxes (the x20 outlier rows).  The lse
-// keeps the fp32 sum of the unrounded values.
+// keeps the fp32 sum of the unrounded values.  The rounded normaliser does
+// not cover every input: when two keys of similar weight dominate a row and
+// the later one exceeds the reference by less than 8, both of their P~ are
+// rounded, and at very sharp softmaxes (scales of about seven times
+// 1/sqrt(d)) the output can pass the element-wise tolerance by up to about
+// a fifth.  A reference kept at the exact running maximum (rescaling on every
+// increase) avoids that at about 6 % of the throughput.
 //
 // gfx950 mapping (this library's design, not the pages'), fwd_bf16_kernel
 // (d = 128; d = 64 runs fwd_small_kernel, further down):
@@ -661,8 +667,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
 //    rescale l, the rounded sum and O~, and take the exponentials again.
 //    Every P~ that reaches the sums is then <= 2^16; the row maximum (16
 //    max3 per lane and tile, a cross-lane step, a ballot) leaves the common
-//    path.  With O~ divided by the sum of the rounded P~, how far the
-//    largest P~ sits from 1 no longer affects the error.
+//    path.  With O~ divided by the sum of the rounded P~, a single dominant
+//    P~ away from 1 costs no accuracy; two near-tied dominant keys still
+//    carry both roundings, as under the lazy rule of the d = 128 kernel.
 constexpr int kSmallTile = 64;
 constexpr float kCheckedSumLimit = 65536.0f;  // 2^16
 
