@@ -325,22 +325,24 @@ def default_splits(B: int, H: int, Nq: int, Nk: int, d: int, H_kv: int | None = 
     """A key-range count for :func:`forward_splitkv`.  With K/V heads shared
     by H / H_kv query heads, fewer than 128 queries per head and every query
     seeing the same keys (no mask, or one query), the library runs a group's
-    rows in one workgroup, and the block count follows that.  Blocks with
-    fewer than 128 rows (decoding) are bound by streaming K and V: about 512
-    workgroups in all (two per compute unit) with ranges of at least 32 key
-    tiles measured best on decode shapes; full blocks are bound by the
-    matrix cores and get about 1024 workgroups with ranges of at least four
-    tiles."""
+    rows in one workgroup, and the block count follows that.  Measured on
+    decode and chunked-prefill shapes, about 512 workgroups in all (two per
+    compute unit) did best.  Blocks with fewer than 128 rows are bound by
+    streaming K and V and keep ranges of at least 32 key tiles, except that
+    fewer than about 256 workgroups may take ranges down to 16 tiles; full
+    blocks keep ranges of at least four tiles."""
     hk = H if H_kv is None else H_kv
     packed = hk < H and Nq < 128 and (Nq == 1 or not causal)
     rows = Nq * (H // hk) if packed else Nq
     blocks = B * (hk if packed else H) * ((rows + 127) // 128)
     tiles = (Nk + 63) // 64  # keys per tile of the bf16 kernels: 64 at both d
+    n = -(-512 // blocks)
     if rows < 128:
-        n, cap = -(-512 // blocks), tiles // 32
+        floor = min(-(-256 // blocks), tiles // 16)
+        n = max(min(n, tiles // 32), floor)
     else:
-        n, cap = -(-1024 // blocks), tiles // 4
-    return int(max(1, min(n, cap, MAX_SPLITS)))
+        n = min(n, tiles // 4)
+    return int(max(1, min(n, MAX_SPLITS)))
 
 
 def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None,

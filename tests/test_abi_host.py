@@ -330,18 +330,25 @@ def test_default_splits():
     # decode (blocks of fewer than 128 rows): about 512 workgroups, ranges of
     # at least 32 key tiles
     assert fa2.default_splits(8, 32, 1, 16384, 128) == 2
-    assert fa2.default_splits(1, 1, 1, 65536, 128) == 32
+    assert fa2.default_splits(1, 1, 1, 65536, 128) == 64  # one head: 64 ranges of 16 tiles
     # grouped decode: a group's query heads share one block
     assert fa2.default_splits(8, 32, 1, 16384, 128, 8, True) == 8
     assert fa2.default_splits(1, 32, 1, 65536, 128, 8, True) == 32
     # a causal mask over several queries keeps the heads apart
     assert fa2.default_splits(8, 32, 4, 16384, 128, 8, True) == 2
+    assert fa2.default_splits(8, 32, 1, 16384, 128, 4, True) == 8
+    # few blocks: at least about 256 workgroups, ranges down to 16 tiles
+    assert fa2.default_splits(2, 32, 16, 16384, 128, 8, False) == 16
     # short keys: never a range below the minimum length
     assert fa2.default_splits(1, 1, 1, 300, 128) == 1
-    # full blocks: about 1024 workgroups, ranges of at least four tiles
+    # full blocks: about 512 workgroups, ranges of at least four tiles
     assert fa2.default_splits(1, 2, 130, 4096, 128) == 16
+    assert fa2.default_splits(1, 16, 512, 32768, 128) == 8
+    assert fa2.default_splits(2, 32, 128, 16384, 128) == 8
+    assert fa2.default_splits(1, 16, 2048, 16384, 128) == 2
     # already enough workgroups: no split
     assert fa2.default_splits(2, 16, 8192, 8192, 128) == 1
+    assert fa2.default_splits(4, 32, 1024, 8192, 128, 8, True) == 1
 
 
 def test_fp8_validation(L):
