@@ -37,6 +37,7 @@ CASES = [
     (1, 2, 2, 300, 128, True),
     (2, 2, 2, 200, 64, False),
     (1, 8, 2, 260, 128, True),
+    (2, 8, 2, 100, 64, False),   # short unmasked grouped blocks: packed forward
 ]
 
 
